@@ -1,0 +1,29 @@
+"""CPU oracle for Multi-Head Latent Attention (MLA) decode — TEST INFRASTRUCTURE.
+
+This package is the slow, plain fp64 definition that the GPU library is
+checked against.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call it; the library in
+``head_latent_attention_13_amd`` never does, and the two share no code.
+
+Modules
+-------
+``expanded``  the method as the pages state it: cache one latent per token,
+              up-project it to per-head keys and values, run causal softmax
+              attention, combine heads with ``W_O``.
+``absorbed``  the same function in its merged-weight form
+              (``W_UQ·W_UKᵀ`` and ``W_UV·W_O``), computed in fp64.  It is
+              pinned to ``expanded`` by the tests and serves as the cheaper
+              reference at sizes where expanding every latent is too slow.
+``rope``      the rotary position embedding used on the decoupled key/query.
+
+Pins (see ``tests/test_oracle_pins.py``): equality with textbook MHA and with
+``torch.nn.functional.scaled_dot_product_attention`` when RoPE is removed,
+absorbed = expanded, softmax invariants, a pure-Python brute force on the
+tiny config, decode = last row of full causal attention, RoPE invariants and
+the byte-count closed forms the pages print.
+
+Parity unpinned (conventions the pages leave open and both sides adopt):
+the RoPE pair layout and frequencies, the source of the query's RoPE part
+(the query latent), and the softmax scale 1/sqrt(d_nope + d_rope).
+"""
+from . import rope, expanded, absorbed, accounting  # noqa: F401

@@ -1,0 +1,179 @@
+"""Seeded input draws for the MLA workloads (no attention arithmetic here).
+
+Everything is drawn from ``numpy.random.default_rng(seed)`` (PCG64) in a
+fixed order so that a (config, seed) pair names one input set:
+
+1. the raw weights ``W_DQ, W_UQ, W_QR, W_DKV, W_KR, W_UK, W_UV, W_O``;
+2. the cached lengths (when the config gives a range);
+3. the page permutation (paged configs);
+4. the history: either cache rows (``history="rows"``) or token activations
+   (``history="x"``), one sequence after another;
+5. the new tokens ``x_new``.
+
+For bf16 configs every value is drawn in fp32 and rounded once to bf16 with
+round-to-nearest-even; both sides consume exactly those values.
+
+Synthetic cache rows stand in for rows appended from real activations: a
+latent ``x @ W_DKV`` with ``x ~ N(0,1)`` and ``W ~ N(0, 0.02^2)`` has entries
+distributed ``N(0, d_model * 0.02^2)``, and the RoPE key is a rotation of an
+identically distributed vector, so rows are drawn i.i.d. from that normal.
+Drawing them directly keeps every decode input independent of the GPU path.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional
+
+import numpy as np
+
+from .configs import MLAConfig
+
+WEIGHT_ORDER = ("W_DQ", "W_UQ", "W_QR", "W_DKV", "W_KR", "W_UK", "W_UV", "W_O")
+
+
+# ---------------------------------------------------------------- bf16 ----
+def bf16_bits(a: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns (uint16), round to nearest even."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    r = ((u >> 16) & 1) + 0x7FFF
+    return ((u + r) >> 16).astype(np.uint16)
+
+
+def bf16_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def round_bf16(a: np.ndarray) -> np.ndarray:
+    """fp32 values rounded to the nearest bf16 value, returned as fp32."""
+    return bf16_to_f32(bf16_bits(a))
+
+
+# ------------------------------------------------------------- shapes ----
+def weight_shapes(cfg: MLAConfig) -> Dict[str, tuple]:
+    H = cfg.n_heads
+    return {
+        "W_DQ": (cfg.d_model, cfg.d_q_latent),
+        "W_UQ": (cfg.d_q_latent, H, cfg.d_nope),
+        "W_QR": (cfg.d_q_latent, H, cfg.d_rope),
+        "W_DKV": (cfg.d_model, cfg.d_latent),
+        "W_KR": (cfg.d_model, cfg.d_rope),
+        "W_UK": (cfg.d_latent, H, cfg.d_nope),
+        "W_UV": (cfg.d_latent, H, cfg.d_v),
+        "W_O": (H, cfg.d_v, cfg.d_model),
+    }
+
+
+def _fan_in(name: str, cfg: MLAConfig) -> int:
+    return {
+        "W_DQ": cfg.d_model, "W_DKV": cfg.d_model, "W_KR": cfg.d_model,
+        "W_UQ": cfg.d_q_latent, "W_QR": cfg.d_q_latent,
+        "W_UK": cfg.d_latent, "W_UV": cfg.d_latent,
+        "W_O": cfg.n_heads * cfg.d_v,
+    }[name]
+
+
+def _finish(a: np.ndarray, cfg: MLAConfig) -> np.ndarray:
+    a = a.astype(np.float32, copy=False)
+    return round_bf16(a) if cfg.dtype == "bf16" else a
+
+
+def _x_std(cfg: MLAConfig) -> float:
+    return (1.0 / cfg.d_model) ** 0.5 if cfg.init == "fanin" else 1.0
+
+
+def row_std(cfg: MLAConfig) -> float:
+    """Std of a latent-cache entry produced from x through W_DKV / W_KR."""
+    if cfg.init == "fanin":
+        return (1.0 / cfg.d_model) ** 0.5
+    return 0.02 * cfg.d_model ** 0.5
+
+
+# -------------------------------------------------------------- draws ----
+def make_weights(cfg: MLAConfig, rng: np.random.Generator) -> Dict[str, np.ndarray]:
+    out = {}
+    for name, shape in weight_shapes(cfg).items():
+        std = (1.0 / _fan_in(name, cfg)) ** 0.5 if cfg.init == "fanin" else 0.02
+        out[name] = _finish(rng.standard_normal(shape, dtype=np.float32) * np.float32(std), cfg)
+    return out
+
+
+def make_lengths(cfg: MLAConfig, rng: np.random.Generator) -> np.ndarray:
+    if isinstance(cfg.cached, tuple):
+        lo, hi = cfg.cached
+        return rng.integers(lo, hi, size=cfg.batch, endpoint=True).astype(np.int64)
+    return np.full(cfg.batch, int(cfg.cached), dtype=np.int64)
+
+
+def make_page_table(kv_len: np.ndarray, page_size: int, rng: np.random.Generator,
+                    spare_pages: int = 0):
+    """Deal a seeded permutation of the shared page pool to the sequences.
+
+    Returns (page_table[B, max_pages] int32 with -1 in unused entries,
+    n_pages).  ``spare_pages`` extra pool pages are left unowned.
+    """
+    pages = [(int(n) + page_size - 1) // page_size for n in kv_len]
+    n_pages = sum(pages) + spare_pages
+    perm = rng.permutation(n_pages).astype(np.int32)
+    max_pages = max(pages) if pages else 0
+    table = np.full((len(pages), max(max_pages, 1)), -1, dtype=np.int32)
+    k = 0
+    for b, n in enumerate(pages):
+        table[b, :n] = perm[k:k + n]
+        k += n
+    return table, n_pages
+
+
+def make_rows(cfg: MLAConfig, lengths: np.ndarray, rng: np.random.Generator) -> List[np.ndarray]:
+    """Synthetic cache rows per sequence, as fp32 arrays [S_b, R]."""
+    std = np.float32(row_std(cfg))
+    return [_finish(rng.standard_normal((int(s), cfg.row), dtype=np.float32) * std, cfg)
+            for s in lengths]
+
+
+def make_x(cfg: MLAConfig, shape, rng: np.random.Generator) -> np.ndarray:
+    return _finish(rng.standard_normal(shape, dtype=np.float32) * np.float32(_x_std(cfg)), cfg)
+
+
+@dataclass
+class Case:
+    cfg: MLAConfig
+    seed: int
+    weights: Dict[str, np.ndarray]
+    cached: np.ndarray                  # [B] cached tokens before this step
+    x_new: np.ndarray                   # [B, n_q, d_model] fp32
+    rows: Optional[List[np.ndarray]] = None       # history rows, history="rows"
+    x_hist: Optional[List[np.ndarray]] = None     # history tokens, history="x"
+    page_table: Optional[np.ndarray] = None
+    n_pages: int = 0
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def kv_len(self) -> np.ndarray:
+        """Visible rows per sequence after the new tokens are appended."""
+        return self.cached + self.cfg.n_q
+
+    @property
+    def positions(self) -> np.ndarray:
+        """[B, n_q] positions of the new tokens (0-based)."""
+        return self.cached[:, None] + np.arange(self.cfg.n_q)[None, :]
+
+
+def make_case(cfg: MLAConfig, seed: int, history: str = "rows",
+              spare_pages: int = 0) -> Case:
+    rng = np.random.default_rng(seed)
+    w = make_weights(cfg, rng)
+    cached = make_lengths(cfg, rng)
+    table, n_pages = (None, 0)
+    if cfg.paged:
+        table, n_pages = make_page_table(cached + cfg.n_q, cfg.page_size, rng, spare_pages)
+    rows = x_hist = None
+    if history == "rows":
+        rows = make_rows(cfg, cached, rng)
+    elif history == "x":
+        x_hist = [make_x(cfg, (int(s), cfg.d_model), rng) for s in cached]
+    else:
+        raise ValueError(history)
+    x_new = make_x(cfg, (cfg.batch, cfg.n_q, cfg.d_model), rng)
+    return Case(cfg=cfg, seed=seed, weights=w, cached=cached, x_new=x_new,
+                rows=rows, x_hist=x_hist, page_table=table, n_pages=n_pages)
