@@ -1,0 +1,404 @@
+// C ABI of the MLA library: argument checks, workspace layout, launches.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "../../include/mla.h"
+#include "mla_common.h"
+#include "mla_internal.h"
+
+using namespace mla;
+
+namespace {
+
+thread_local char g_err[512];
+
+mla_status fail(mla_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+mla_status hip_fail(hipError_t e, const char* what) {
+  return fail(MLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+bool is_bf16(const mla_dims* d) { return d->dtype == MLA_BF16; }
+int esize(const mla_dims* d) { return is_bf16(d) ? 2 : 4; }
+int row_width(const mla_dims* d) { return d->d_latent + d->d_rope; }
+
+mla_status check_dims(const mla_dims* d) {
+  if (!d) return fail(MLA_ERR_INVALID_ARG, "dims is NULL");
+  if (d->d_model <= 0 || d->n_heads <= 0 || d->d_latent <= 0 || d->d_q_latent <= 0 || d->d_nope <= 0 ||
+      d->d_rope <= 0 || d->d_v <= 0)
+    return fail(MLA_ERR_INVALID_ARG, "all dimensions must be positive");
+  if (d->dtype != MLA_F32 && d->dtype != MLA_BF16) return fail(MLA_ERR_INVALID_ARG, "dtype %d", d->dtype);
+  if ((d->d_rope & 1) || (d->d_latent & 1)) return fail(MLA_ERR_INVALID_ARG, "d_rope and d_latent must be even");
+  if (!(d->rope_base > 0.f)) return fail(MLA_ERR_INVALID_ARG, "rope_base must be > 0");
+  if (d->softmax_scale < 0.f || !isfinite(d->softmax_scale)) return fail(MLA_ERR_INVALID_ARG, "softmax_scale");
+  const int KB = is_bf16(d) ? 32 : 4;
+  if (d->d_model % KB || d->d_q_latent % KB || (d->n_heads * d->d_latent) % KB)
+    return fail(MLA_ERR_UNSUPPORTED, "d_model, d_q_latent and n_heads*d_latent must be multiples of %d", KB);
+  return MLA_OK;
+}
+
+mla_status check_attn_dims(const mla_dims* d) {
+  if (!attn_supported(is_bf16(d), d->n_heads, d->d_latent, d->d_rope))
+    return fail(MLA_ERR_UNSUPPORTED,
+                "no attention kernel for dtype=%d H=%d d_latent=%d d_rope=%d (built: bf16 512+64, fp32 32+8)",
+                d->dtype, d->n_heads, d->d_latent, d->d_rope);
+  return MLA_OK;
+}
+
+float scale_of(const mla_dims* d) {
+  return d->softmax_scale > 0.f ? d->softmax_scale : 1.0f / sqrtf((float)(d->d_nope + d->d_rope));
+}
+
+// ---------------------------------------------------------- absorbed ----
+struct AbsLayout {
+  size_t off[4], bytes[4], total;
+};
+
+AbsLayout abs_layout(const mla_dims* d) {
+  const int KB = is_bf16(d) ? 32 : 4, R = row_width(d);
+  const int K[4] = {d->d_model, d->d_model, d->d_q_latent, d->n_heads * d->d_latent};
+  const int N[4] = {R, d->d_q_latent, d->n_heads * R, d->d_model};
+  AbsLayout L{};
+  size_t o = 0;
+  for (int i = 0; i < 4; ++i) {
+    L.off[i] = o;
+    L.bytes[i] = (size_t)ceil_div(K[i], KB) * KB * (size_t)ceil_div(N[i], 16) * 16 * esize(d);
+    o = align256(o + L.bytes[i]);
+  }
+  L.total = o;
+  return L;
+}
+
+// ---------------------------------------------------------- workspace ----
+struct WsLayout {
+  size_t err, q, cq, part, tile_off, attn_o, attn_lse, total;
+  GemmPlan g_app, g_cq, g_q, g_out;
+  int G, V;
+};
+
+WsLayout ws_layout(const mla_dims* d, int batch, int n_q) {
+  WsLayout W{};
+  const bool bf = is_bf16(d);
+  const int M = batch * n_q, R = row_width(d), H = d->n_heads;
+  const int ncu = device_cus();
+  W.g_app = plan_gemm(M, d->d_model, R, bf, ncu);
+  W.g_cq = plan_gemm(M, d->d_model, d->d_q_latent, bf, ncu);
+  W.g_q = plan_gemm(M, d->d_q_latent, H * R, bf, ncu);
+  W.g_out = plan_gemm(M, H * d->d_latent, d->d_model, bf, ncu);
+  W.G = ncu;
+  W.V = M;
+  size_t o = 0;
+  W.err = o; o = align256(o + 256);
+  W.q = o; o = align256(o + (size_t)M * H * R * esize(d));
+  W.cq = o; o = align256(o + (size_t)M * d->d_q_latent * esize(d));
+  size_t part = std::max(std::max(W.g_app.part_bytes, W.g_cq.part_bytes), std::max(W.g_q.part_bytes, W.g_out.part_bytes));
+  W.part = o; o = align256(o + part);
+  const int HG = attn_head_group(bf);
+  const size_t U = (size_t)M * ((H + HG - 1) / HG);
+  W.tile_off = o; o = align256(o + (U + 1) * 4);
+  const size_t slots = (size_t)W.G + U;
+  W.attn_o = o; o = align256(o + slots * HG * d->d_latent * 4);
+  W.attn_lse = o; o = align256(o + slots * HG * 4);
+  W.total = o;
+  return W;
+}
+
+mla_status check_ws(const WsLayout& W, void* ws, size_t ws_bytes) {
+  if (!ws) return fail(MLA_ERR_INVALID_ARG, "workspace is NULL");
+  if (!aligned(ws, 256)) return fail(MLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (ws_bytes < W.total) return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, W.total);
+  return MLA_OK;
+}
+
+mla_status check_cache(const mla_dims* d, const mla_cache* c, int batch) {
+  if (!c || !c->pool) return fail(MLA_ERR_INVALID_ARG, "cache or cache->pool is NULL");
+  if (!aligned(c->pool, 16)) return fail(MLA_ERR_INVALID_ARG, "cache pool must be 16-byte aligned");
+  if (c->page_table) {
+    if (c->page_size <= 0 || c->page_size % 32) return fail(MLA_ERR_INVALID_ARG, "page_size must be a positive multiple of 32");
+    if (c->n_pages <= 0 || c->max_pages_per_seq <= 0) return fail(MLA_ERR_INVALID_ARG, "n_pages / max_pages_per_seq");
+    if ((long)c->max_pages_per_seq * c->page_size > (long)INT32_MAX) return fail(MLA_ERR_INVALID_ARG, "capacity overflow");
+  } else {
+    if (c->s_max <= 0) return fail(MLA_ERR_INVALID_ARG, "contiguous cache needs s_max > 0");
+  }
+  (void)d;
+  (void)batch;
+  return MLA_OK;
+}
+
+mla_status run_gemm(const GemmPlan& g, bool bf16, bool a_f32, const void* A, int lda, const void* Wp, float* part,
+                    hipStream_t s) {
+  hipError_t e = launch_gemm(g, bf16, a_f32, A, lda, Wp, part, s);
+  if (e != hipSuccess) return hip_fail(e, "gemm launch");
+  return MLA_OK;
+}
+
+EpiArgs base_epi(const GemmPlan& g, int mode, const float* part, void* out) {
+  EpiArgs e{};
+  e.mode = mode;
+  e.M = g.M; e.N = g.N; e.Np = g.Np; e.ksplit = g.ksplit;
+  e.part = part;
+  e.out = out;
+  return e;
+}
+
+mla_status q_proj_impl(const mla_dims* d, const WsLayout& W, const unsigned char* abs, const void* x,
+                       const int32_t* kv_len, int batch, int n_q, void* q, unsigned char* ws, hipStream_t s) {
+  const bool bf = is_bf16(d);
+  const AbsLayout L = abs_layout(d);
+  float* part = reinterpret_cast<float*>(ws + W.part);
+  void* cq = ws + W.cq;
+  mla_status st = run_gemm(W.g_cq, bf, false, x, d->d_model, abs + L.off[1], part, s);
+  if (st) return st;
+  EpiArgs e = base_epi(W.g_cq, EPI_STORE_T, part, cq);
+  hipError_t he = launch_epilogue(e, bf, s);
+  if (he != hipSuccess) return hip_fail(he, "epilogue launch");
+  st = run_gemm(W.g_q, bf, false, cq, d->d_q_latent, abs + L.off[2], part, s);
+  if (st) return st;
+  e = base_epi(W.g_q, EPI_Q, part, q);
+  e.d_latent = d->d_latent; e.d_rope = d->d_rope; e.row = row_width(d); e.rope_base = d->rope_base;
+  e.n_q = n_q; e.kv_len = kv_len;
+  he = launch_epilogue(e, bf, s);
+  if (he != hipSuccess) return hip_fail(he, "epilogue launch");
+  (void)batch;
+  return MLA_OK;
+}
+
+mla_status attention_impl(const mla_dims* d, const WsLayout& W, const void* q, const int32_t* kv_len, int batch,
+                          int n_q, const mla_cache* c, float* o_lat, float* lse, unsigned char* ws, hipStream_t s) {
+  AttnArgs a{};
+  a.q = q;
+  a.pool = c->pool;
+  a.page_table = c->page_table;
+  a.paged = c->page_table != nullptr;
+  a.page_size = a.paged ? c->page_size : 32;
+  a.n_pages = c->n_pages;
+  a.max_pages = c->max_pages_per_seq;
+  a.s_max = c->s_max;
+  a.kv_len = kv_len;
+  a.B = batch;
+  a.n_q = n_q;
+  a.H = d->n_heads;
+  a.V = batch * n_q;
+  a.tile_off = reinterpret_cast<int32_t*>(ws + W.tile_off);
+  a.o_lat = o_lat;
+  a.lse = lse;
+  a.part_o = reinterpret_cast<float*>(ws + W.attn_o);
+  a.part_lse = reinterpret_cast<float*>(ws + W.attn_lse);
+  a.err = reinterpret_cast<int32_t*>(ws + W.err);
+  a.scale_log2 = scale_of(d) * 1.4426950408889634f;
+  a.G = W.G;
+  hipError_t e = launch_attention(a, is_bf16(d), s);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return MLA_OK;
+}
+
+mla_status check_common(const mla_dims* d, const void* absorbed, int batch, int n_q) {
+  mla_status st = check_dims(d);
+  if (st) return st;
+  if (absorbed && !aligned(absorbed, 256)) return fail(MLA_ERR_INVALID_ARG, "absorbed buffer must be 256-byte aligned");
+  if (batch <= 0 || n_q <= 0) return fail(MLA_ERR_INVALID_ARG, "batch (%d) and n_q (%d) must be positive", batch, n_q);
+  if ((long)batch * n_q > (1L << 24)) return fail(MLA_ERR_INVALID_ARG, "batch*n_q too large");
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_str(int32_t s) {
+  switch (s) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE";
+    default: return "MLA_ERR_UNKNOWN";
+  }
+}
+
+const char* mla_last_error(void) { return g_err; }
+
+const char* mla_version(void) { return "mla-gfx950 0.1"; }
+
+mla_status mla_absorbed_layout(const mla_dims* d, size_t offsets[4], size_t bytes[4], size_t* total) {
+  mla_status st = check_dims(d);
+  if (st) return st;
+  if (!total) return fail(MLA_ERR_INVALID_ARG, "total is NULL");
+  const AbsLayout L = abs_layout(d);
+  for (int i = 0; i < 4; ++i) {
+    if (offsets) offsets[i] = L.off[i];
+    if (bytes) bytes[i] = L.bytes[i];
+  }
+  *total = L.total;
+  return MLA_OK;
+}
+
+mla_status mla_absorb_weights(const mla_dims* d, const mla_raw_weights* raw, void* absorbed, size_t absorbed_bytes,
+                              void* stream) {
+  mla_status st = check_dims(d);
+  if (st) return st;
+  if (!raw || !raw->W_DQ || !raw->W_UQ || !raw->W_QR || !raw->W_DKV || !raw->W_KR || !raw->W_UK || !raw->W_UV ||
+      !raw->W_O)
+    return fail(MLA_ERR_INVALID_ARG, "a raw weight pointer is NULL");
+  if (!absorbed || !aligned(absorbed, 256)) return fail(MLA_ERR_INVALID_ARG, "absorbed must be non-NULL and 256-byte aligned");
+  const AbsLayout L = abs_layout(d);
+  if (absorbed_bytes < L.total) return fail(MLA_ERR_WORKSPACE, "absorbed %zu bytes < %zu needed", absorbed_bytes, L.total);
+  unsigned char* ab = reinterpret_cast<unsigned char*>(absorbed);
+  AbsorbArgs a{};
+  a.d_model = d->d_model; a.H = d->n_heads; a.d_latent = d->d_latent; a.d_q_latent = d->d_q_latent;
+  a.d_nope = d->d_nope; a.d_rope = d->d_rope; a.d_v = d->d_v;
+  a.W_DQ = raw->W_DQ; a.W_UQ = raw->W_UQ; a.W_QR = raw->W_QR; a.W_DKV = raw->W_DKV; a.W_KR = raw->W_KR;
+  a.W_UK = raw->W_UK; a.W_UV = raw->W_UV; a.W_O = raw->W_O;
+  a.P_KV = ab + L.off[0]; a.P_DQ = ab + L.off[1]; a.P_QC = ab + L.off[2]; a.P_O = ab + L.off[3];
+  hipError_t e = launch_absorb(a, is_bf16(d), reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "absorb launch");
+  return MLA_OK;
+}
+
+mla_status mla_workspace_size(const mla_dims* d, int32_t batch, int32_t n_q, size_t* bytes) {
+  mla_status st = check_common(d, nullptr, batch, n_q);
+  if (st) return st;
+  if (!bytes) return fail(MLA_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = ws_layout(d, batch, n_q).total;
+  return MLA_OK;
+}
+
+mla_status mla_read_device_error(void* workspace, int32_t* flags, void* stream) {
+  if (!workspace || !flags) return fail(MLA_ERR_INVALID_ARG, "workspace and flags must be non-NULL");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  int32_t h = 0;
+  hipError_t e = hipMemcpyAsync(&h, workspace, sizeof(int32_t), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "reading the device error word");
+  const int32_t zero = 0;
+  e = hipMemcpyAsync(workspace, &zero, sizeof(int32_t), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "clearing the device error word");
+  *flags = h;
+  return MLA_OK;
+}
+
+mla_status mla_compress_append(const mla_dims* d, const void* absorbed, const void* x, const int32_t* pos,
+                               int32_t batch, int32_t n_q, const mla_cache* cache, void* workspace, size_t ws_bytes,
+                               void* stream) {
+  mla_status st = check_common(d, absorbed, batch, n_q);
+  if (st) return st;
+  if (!absorbed || !x || !pos) return fail(MLA_ERR_INVALID_ARG, "absorbed, x and pos must be non-NULL");
+  if (!aligned(x, 16)) return fail(MLA_ERR_INVALID_ARG, "x must be 16-byte aligned");
+  if ((st = check_cache(d, cache, batch))) return st;
+  const WsLayout W = ws_layout(d, batch, n_q);
+  if ((st = check_ws(W, workspace, ws_bytes))) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const bool bf = is_bf16(d);
+  const AbsLayout L = abs_layout(d);
+  unsigned char* ws = reinterpret_cast<unsigned char*>(workspace);
+  float* part = reinterpret_cast<float*>(ws + W.part);
+  st = run_gemm(W.g_app, bf, false, x, d->d_model, reinterpret_cast<const unsigned char*>(absorbed) + L.off[0], part, s);
+  if (st) return st;
+  EpiArgs e = base_epi(W.g_app, EPI_APPEND, part, nullptr);
+  e.d_latent = d->d_latent; e.d_rope = d->d_rope; e.row = row_width(d); e.rope_base = d->rope_base;
+  e.n_q = n_q; e.pos = pos;
+  e.pool = cache->pool; e.page_table = cache->page_table; e.paged = cache->page_table != nullptr;
+  e.page_size = cache->page_size; e.n_pages = cache->n_pages; e.max_pages = cache->max_pages_per_seq;
+  e.s_max = cache->s_max;
+  e.err = reinterpret_cast<int32_t*>(ws + W.err);
+  hipError_t he = launch_epilogue(e, bf, s);
+  if (he != hipSuccess) return hip_fail(he, "append launch");
+  return MLA_OK;
+}
+
+mla_status mla_q_proj(const mla_dims* d, const void* absorbed, const void* x, const int32_t* kv_len, int32_t batch,
+                      int32_t n_q, void* q, void* workspace, size_t ws_bytes, void* stream) {
+  mla_status st = check_common(d, absorbed, batch, n_q);
+  if (st) return st;
+  if (!absorbed || !x || !kv_len || !q) return fail(MLA_ERR_INVALID_ARG, "absorbed, x, kv_len and q must be non-NULL");
+  if (!aligned(x, 16) || !aligned(q, 16)) return fail(MLA_ERR_INVALID_ARG, "x and q must be 16-byte aligned");
+  const WsLayout W = ws_layout(d, batch, n_q);
+  if ((st = check_ws(W, workspace, ws_bytes))) return st;
+  return q_proj_impl(d, W, reinterpret_cast<const unsigned char*>(absorbed), x, kv_len, batch, n_q, q,
+                     reinterpret_cast<unsigned char*>(workspace), reinterpret_cast<hipStream_t>(stream));
+}
+
+mla_status mla_attention(const mla_dims* d, const void* q, const int32_t* kv_len, int32_t batch, int32_t n_q,
+                         const mla_cache* cache, float* o_lat, float* lse, void* workspace, size_t ws_bytes,
+                         void* stream) {
+  mla_status st = check_common(d, nullptr, batch, n_q);
+  if (st) return st;
+  if ((st = check_attn_dims(d))) return st;
+  if (!q || !kv_len || !o_lat) return fail(MLA_ERR_INVALID_ARG, "q, kv_len and o_lat must be non-NULL");
+  if (!aligned(q, 16) || !aligned(o_lat, 16) || (lse && !aligned(lse, 4)))
+    return fail(MLA_ERR_INVALID_ARG, "q and o_lat must be 16-byte aligned");
+  if ((st = check_cache(d, cache, batch))) return st;
+  const WsLayout W = ws_layout(d, batch, n_q);
+  if ((st = check_ws(W, workspace, ws_bytes))) return st;
+  return attention_impl(d, W, q, kv_len, batch, n_q, cache, o_lat, lse, reinterpret_cast<unsigned char*>(workspace),
+                        reinterpret_cast<hipStream_t>(stream));
+}
+
+mla_status mla_decode(const mla_dims* d, const void* absorbed, const void* x, const int32_t* kv_len, int32_t batch,
+                      int32_t n_q, const mla_cache* cache, float* o_lat, float* lse, void* workspace, size_t ws_bytes,
+                      void* stream) {
+  mla_status st = check_common(d, absorbed, batch, n_q);
+  if (st) return st;
+  if ((st = check_attn_dims(d))) return st;
+  if (!absorbed || !x || !kv_len || !o_lat) return fail(MLA_ERR_INVALID_ARG, "absorbed, x, kv_len and o_lat must be non-NULL");
+  if (!aligned(x, 16) || !aligned(o_lat, 16)) return fail(MLA_ERR_INVALID_ARG, "x and o_lat must be 16-byte aligned");
+  if ((st = check_cache(d, cache, batch))) return st;
+  const WsLayout W = ws_layout(d, batch, n_q);
+  if ((st = check_ws(W, workspace, ws_bytes))) return st;
+  unsigned char* ws = reinterpret_cast<unsigned char*>(workspace);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  st = q_proj_impl(d, W, reinterpret_cast<const unsigned char*>(absorbed), x, kv_len, batch, n_q, ws + W.q, ws, s);
+  if (st) return st;
+  return attention_impl(d, W, ws + W.q, kv_len, batch, n_q, cache, o_lat, lse, ws, s);
+}
+
+mla_status mla_out_proj(const mla_dims* d, const void* absorbed, const float* o_lat, int32_t n_tok, float* y,
+                        void* workspace, size_t ws_bytes, void* stream) {
+  mla_status st = check_common(d, absorbed, n_tok, 1);
+  if (st) return st;
+  if (!absorbed || !o_lat || !y) return fail(MLA_ERR_INVALID_ARG, "absorbed, o_lat and y must be non-NULL");
+  if (!aligned(o_lat, 16) || !aligned(y, 16)) return fail(MLA_ERR_INVALID_ARG, "o_lat and y must be 16-byte aligned");
+  const WsLayout W = ws_layout(d, n_tok, 1);
+  if ((st = check_ws(W, workspace, ws_bytes))) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const bool bf = is_bf16(d);
+  const AbsLayout L = abs_layout(d);
+  unsigned char* ws = reinterpret_cast<unsigned char*>(workspace);
+  float* part = reinterpret_cast<float*>(ws + W.part);
+  st = run_gemm(W.g_out, bf, true, o_lat, d->n_heads * d->d_latent, reinterpret_cast<const unsigned char*>(absorbed) + L.off[3],
+                part, s);
+  if (st) return st;
+  EpiArgs e = base_epi(W.g_out, EPI_F32, part, y);
+  hipError_t he = launch_epilogue(e, bf, s);
+  if (he != hipSuccess) return hip_fail(he, "epilogue launch");
+  return MLA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,84 @@
+// Host-side interfaces between the C ABI (mla_api.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla {
+
+// ---------------------------------------------------------------- GEMM ----
+// y[M][N] = A[M][K] * W[K][N] with W in the packed fragment layout.
+// Work split: n-groups of NT 16-column tiles, m-groups of MT 16-row tiles,
+// ksplit slices of the K range.  fp32 partial sums go to part[ks][M][Np].
+struct GemmPlan {
+  int M, K, N;       // logical sizes
+  int Kp, Np;        // padded sizes of the packed weight
+  int KB;            // k per MFMA (32 bf16, 4 fp32)
+  int kblocks, ntiles;
+  int NT, MT, ngroups, mgroups;
+  int ksplit, kb_per_split;
+  size_t part_bytes;
+};
+
+GemmPlan plan_gemm(int M, int K, int N, bool bf16, int n_cu);
+
+// A is T (a_f32 == false) or fp32 (a_f32 == true); Wp is T.
+hipError_t launch_gemm(const GemmPlan& g, bool bf16, bool a_f32, const void* A, int lda,
+                       const void* Wp, float* part, hipStream_t s);
+
+enum EpiMode { EPI_F32 = 0, EPI_STORE_T = 1, EPI_Q = 2, EPI_APPEND = 3 };
+
+struct EpiArgs {
+  int mode;
+  int M, N, Np, ksplit;
+  const float* part;
+  void* out;            // EPI_F32: float[M][N]; EPI_STORE_T / EPI_Q: T[M][N]
+  // RoPE (EPI_Q, EPI_APPEND)
+  int d_latent, d_rope, row;   // row = d_latent + d_rope
+  float rope_base;
+  int n_q;
+  const int32_t* kv_len;       // EPI_Q: query t of sequence b sits at kv_len[b]-n_q+t
+  const int32_t* pos;          // EPI_APPEND: token t of sequence b sits at pos[b]+t
+  // cache (EPI_APPEND)
+  void* pool;
+  const int32_t* page_table;
+  int paged, page_size, n_pages, max_pages, s_max;
+  int32_t* err;
+};
+
+hipError_t launch_epilogue(const EpiArgs& e, bool bf16, hipStream_t s);
+
+// ------------------------------------------------------------- absorb ----
+struct AbsorbArgs {
+  int d_model, H, d_latent, d_q_latent, d_nope, d_rope, d_v;
+  const void *W_DQ, *W_UQ, *W_QR, *W_DKV, *W_KR, *W_UK, *W_UV, *W_O;
+  void *P_KV, *P_DQ, *P_QC, *P_O;   // packed outputs
+};
+hipError_t launch_absorb(const AbsorbArgs& a, bool bf16, hipStream_t s);
+
+// ---------------------------------------------------------- attention ----
+struct AttnArgs {
+  const void* q;               // [V][H][R]
+  const void* pool;
+  const int32_t* page_table;
+  int paged, page_size, n_pages, max_pages, s_max;
+  const int32_t* kv_len;
+  int B, n_q, H, V;
+  int n_hg, U;                 // head groups per query row; streams U = V * n_hg (set by the launcher)
+  int32_t* tile_off;           // [U+1]  (written by the plan kernel)
+  float* o_lat;                // [V][H][d_latent]
+  float* lse;                  // [V][H] natural-log LSE of scaled scores, or null
+  float* part_o;               // [(G+U)][head group][d_latent]
+  float* part_lse;             // [(G+U)][head group]
+  int32_t* err;
+  float scale_log2;            // softmax scale * log2(e)
+  int G;                       // attention work-groups
+};
+
+int attn_supported(bool bf16, int H, int d_latent, int d_rope);
+int attn_head_group(bool bf16);  // heads per attention work-group
+int attn_tile();
+hipError_t launch_attention(const AttnArgs& a, bool bf16, hipStream_t s);
+
+}  // namespace mla

@@ -46,10 +46,10 @@ def query_latent(W: Dict[str, np.ndarray], uqk: np.ndarray, x: np.ndarray, pos,
     """q_lat [n, Hs, d_L] and q_pe [n, Hs, d_rope] for tokens x at ``pos``."""
     x = _f64(x)
     c_q = x @ _f64(W["W_DQ"])
-    q_lat = np.einsum("nl,hlc->nhc", c_q, uqk)
+    q_lat = np.einsum("nl,hlc->nhc", c_q, uqk, optimize=True)
     W_QR = _f64(W["W_QR"])
     hs = list(range(W_QR.shape[1])) if heads is None else list(heads)
-    q_pe = _rope.apply(np.einsum("nl,lhr->nhr", c_q, W_QR[:, hs, :]),
+    q_pe = _rope.apply(np.einsum("nl,lhr->nhr", c_q, W_QR[:, hs, :], optimize=True),
                        np.asarray(pos)[:, None], base)
     return q_lat, q_pe
 
@@ -61,19 +61,20 @@ def attention(q_lat: np.ndarray, q_pe: np.ndarray, c: np.ndarray, k_pe: np.ndarr
     q_pos = np.asarray(q_pos, dtype=np.int64)
     m = c.shape[0]
     visible = np.arange(m)[None, None, :] <= q_pos[:, None, None]   # [n, 1, m]
-    s = (np.einsum("nhc,mc->nhm", q_lat, c) + np.einsum("nhr,mr->nhm", q_pe, k_pe)) * scale
+    s = (np.einsum("nhc,mc->nhm", q_lat, c, optimize=True)
+         + np.einsum("nhr,mr->nhm", q_pe, k_pe, optimize=True)) * scale
     s = np.where(visible, s, -np.inf)
     mx = s.max(axis=2, keepdims=True)
     e = np.exp(s - mx)
     den = e.sum(axis=2, keepdims=True)
     p = e / den
-    o_lat = np.einsum("nhm,mc->nhc", p, c)
+    o_lat = np.einsum("nhm,mc->nhc", p, c, optimize=True)
     out = {"o_lat": o_lat, "lse": mx[..., 0] + np.log(den[..., 0])}
     if uvo is not None:
-        out["y"] = np.einsum("nhc,hcd->nd", o_lat, uvo)
+        out["y"] = np.einsum("nhc,hcd->nd", o_lat, uvo, optimize=True)
     return out
 
 
 def out_proj(o_lat: np.ndarray, uvo: np.ndarray) -> np.ndarray:
     """y [n, d_model] = sum_h o_lat[:, h] W_UVO[h]."""
-    return np.einsum("nhc,hcd->nd", _f64(o_lat), uvo)
+    return np.einsum("nhc,hcd->nd", _f64(o_lat), uvo, optimize=True)

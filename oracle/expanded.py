@@ -60,8 +60,9 @@ def query(W: Dict[str, np.ndarray], x: np.ndarray, pos, base: float):
     """
     x = _f64(x)
     c_q = x @ _f64(W["W_DQ"])
-    q_nope = np.einsum("nl,lhd->nhd", c_q, _f64(W["W_UQ"]))
-    q_rot = np.einsum("nl,lhr->nhr", c_q, _f64(W["W_QR"]))
+    W_UQ, W_QR = _f64(W["W_UQ"]), _f64(W["W_QR"])
+    q_nope = (c_q @ W_UQ.reshape(W_UQ.shape[0], -1)).reshape(len(c_q), *W_UQ.shape[1:])
+    q_rot = (c_q @ W_QR.reshape(W_QR.shape[0], -1)).reshape(len(c_q), *W_QR.shape[1:])
     q_pe = _rope.apply(q_rot, np.asarray(pos)[:, None], base)
     return c_q, q_nope, q_pe
 
@@ -104,8 +105,10 @@ def attention(W: Dict[str, np.ndarray], q_nope: np.ndarray, q_pe: np.ndarray,
     y = np.zeros((n, d_model))
     for s in range(0, len(hs), head_block):
         blk = hs[s:s + head_block]
-        k_nope = np.einsum("ml,lhd->hmd", c, W_UK[:, blk, :])        # [hb, m, d_nope]
-        v = np.einsum("ml,lhd->hmd", c, W_UV[:, blk, :])             # [hb, m, d_v]
+        hb = len(blk)
+        # up-project every visible latent to this block's per-head keys/values
+        k_nope = (c @ W_UK[:, blk, :].reshape(d_L, -1)).reshape(m, hb, -1).transpose(1, 0, 2)  # [hb, m, d_nope]
+        v = (c @ W_UV[:, blk, :].reshape(d_L, -1)).reshape(m, hb, -1).transpose(1, 0, 2)       # [hb, m, d_v]
         qn = q_nope[:, blk, :].transpose(1, 0, 2)                    # [hb, n, d_nope]
         qp = q_pe[:, blk, :].transpose(1, 0, 2)                      # [hb, n, d_rope]
         scores = (qn @ k_nope.transpose(0, 2, 1)) + (qp @ k_pe.T[None])  # [hb, n, m]
@@ -122,7 +125,7 @@ def attention(W: Dict[str, np.ndarray], q_nope: np.ndarray, q_pe: np.ndarray,
         if want_p:
             p_all[:, s:s + len(blk)] = p.transpose(1, 0, 2)
         if want_y:
-            y += np.einsum("hnd,hdm->nm", ob, W_O[blk])
+            y += ob.transpose(1, 0, 2).reshape(n, -1) @ W_O[blk].reshape(hb * d_v, d_model)
     out = {"o_h": o_h, "o_lat": o_lat, "lse": lse}
     if want_p:
         out["p"] = p_all

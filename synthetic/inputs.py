@@ -33,11 +33,12 @@ WEIGHT_ORDER = ("W_DQ", "W_UQ", "W_QR", "W_DKV", "W_KR", "W_UK", "W_UV", "W_O")
 
 # ---------------------------------------------------------------- bf16 ----
 def bf16_bits(a: np.ndarray) -> np.ndarray:
-    """fp32 -> bf16 bit patterns (uint16), round to nearest even."""
-    a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    r = ((u >> 16) & 1) + 0x7FFF
-    return ((u + r) >> 16).astype(np.uint16)
+    """fp32 -> bf16 bit patterns (uint16), round to nearest even (finite inputs)."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    r = (u >> np.uint32(16)) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u  # no overflow for finite values below the largest bf16 binade
+    return (r >> np.uint32(16)).astype(np.uint16)
 
 
 def bf16_to_f32(b: np.ndarray) -> np.ndarray:

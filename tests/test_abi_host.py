@@ -1,0 +1,135 @@
+"""Host-side checks of the C ABI library (no GPU work is enqueued).
+
+The library must load, export every entry point declared in include/mla.h,
+and reject bad arguments on the host before anything reaches a stream.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+
+mla = pytest.importorskip("head_latent_attention_13_amd")
+
+
+def _lib():
+    if not os.path.exists(mla.LIB_PATH):
+        pytest.skip("libmla.so not built (run __graft_entry__.build())")
+    return mla.load()
+
+
+def declared_symbols():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_four_hot_path_calls():
+    syms = declared_symbols()
+    for s in ("mla_absorb_weights", "mla_compress_append", "mla_decode", "mla_out_proj"):
+        assert s in syms
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    missing = [s for s in declared_symbols() if not hasattr(lib, s)]
+    assert not missing, missing
+    assert set(declared_symbols()) == set(mla.EXPORTED)
+
+
+def test_status_strings_and_version():
+    lib = _lib()
+    assert lib.mla_status_str(0) == b"MLA_OK"
+    assert lib.mla_status_str(-4) == b"MLA_ERR_WORKSPACE"
+    assert mla.mla_version().startswith("mla-gfx950")
+
+
+def v2_dims(dtype="bf16"):
+    return mla.make_dims(5120, 128, 512, 1536, 128, 64, 128, dtype)
+
+
+def test_absorbed_layout_sizes_v2():
+    _lib()
+    offs, sizes, total = mla.mla_absorbed_layout(v2_dims())
+    R, H = 576, 128
+    assert sizes == [5120 * R * 2, 5120 * 1536 * 2, 1536 * H * R * 2, H * 512 * 5120 * 2]
+    assert all(o % 256 == 0 for o in offs) and offs == sorted(offs)
+    assert total >= offs[3] + sizes[3]
+
+
+def test_absorbed_layout_pads_fp32_tiny():
+    _lib()
+    offs, sizes, total = mla.mla_absorbed_layout(mla.make_dims(64, 4, 32, 48, 16, 8, 16, "f32"))
+    # N = 40 rounds up to 48 columns; K multiples of 4 need no padding
+    assert sizes[0] == 64 * 48 * 4
+    assert sizes[2] == 48 * 160 * 4
+
+
+def test_workspace_size_grows_with_batch():
+    _lib()
+    d = v2_dims()
+    assert mla.mla_workspace_size(d, 64, 1) > mla.mla_workspace_size(d, 16, 1) > 0
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("d_model", 0, -1), ("d_rope", 63, -1), ("dtype", 7, -1), ("d_model", 5100, -2), ("rope_base", 0.0, -1),
+])
+def test_bad_dims_rejected(field, value, code):
+    _lib()
+    d = v2_dims()
+    setattr(d, field, value)
+    with pytest.raises(mla.MLAError) as e:
+        mla.mla_workspace_size(d, 16, 1)
+    assert e.value.status == code
+
+
+def test_null_and_misaligned_pointers_rejected_before_launch():
+    lib = _lib()
+    d = v2_dims()
+    cache = mla._lib.mla_cache(0x1000, None, 0, 0, 0, 4097)
+    ws = ctypes.c_void_p(0x100000)
+    # NULL x
+    st = lib.mla_decode(ctypes.byref(d), ctypes.c_void_p(0x1000), None, ctypes.c_void_p(0x2000), 16, 1,
+                        ctypes.byref(cache), ctypes.c_void_p(0x3000), None, ws, 1 << 40, None)
+    assert st == -1
+    # misaligned x
+    st = lib.mla_decode(ctypes.byref(d), ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1002), ctypes.c_void_p(0x2000),
+                        16, 1, ctypes.byref(cache), ctypes.c_void_p(0x3000), None, ws, 1 << 40, None)
+    assert st == -1
+    # workspace too small
+    st = lib.mla_decode(ctypes.byref(d), ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000),
+                        16, 1, ctypes.byref(cache), ctypes.c_void_p(0x3000), None, ws, 1024, None)
+    assert st == -4
+    # paged cache with a page size that is not a multiple of 32
+    bad = mla._lib.mla_cache(0x1000, 0x2000, 48, 10, 4, 0)
+    st = lib.mla_attention(ctypes.byref(d), ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000), 16, 1,
+                           ctypes.byref(bad), ctypes.c_void_p(0x3000), None, ws, 1 << 40, None)
+    assert st == -1
+    # batch <= 0
+    st = lib.mla_out_proj(ctypes.byref(d), ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1000), 0,
+                          ctypes.c_void_p(0x3000), ws, 1 << 40, None)
+    assert st == -1
+    assert lib.mla_last_error()
+
+
+def test_attention_dims_without_a_kernel_are_unsupported():
+    lib = _lib()
+    d = mla.make_dims(5120, 128, 256, 1536, 128, 64, 128, "bf16")  # d_latent 256: no kernel built
+    cache = mla._lib.mla_cache(0x1000, None, 0, 0, 0, 100)
+    st = lib.mla_attention(ctypes.byref(d), ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000), 1, 1,
+                           ctypes.byref(cache), ctypes.c_void_p(0x3000), None, ctypes.c_void_p(0x100000), 1 << 40,
+                           None)
+    assert st == -2
+
+
+def test_synthetic_bf16_rounding_matches_torch():
+    import torch
+    from synthetic import round_bf16
+    a = np.random.default_rng(0).standard_normal(100000).astype(np.float32) * 3
+    a[:4] = [1.00390625, 1.01171875, -2.00390625, 0.0]  # exact ties
+    ref = torch.from_numpy(a).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(round_bf16(a), ref)

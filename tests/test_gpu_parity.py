@@ -1,0 +1,299 @@
+"""GPU path vs the CPU oracle, through the C ABI (MI355X only).
+
+Every input comes from the seeded generators in ``synthetic``; expected
+values come from ``oracle`` (fp64).  Tolerances: rel-L2 <= 1e-2 and
+max-abs <= 3e-2 for bf16 caches with fp32 accumulation; 1e-5 for the fp32
+configuration; bit-exact for cache placement and page-table gathering.
+Large configurations are compared on sampled sequences / heads / query
+tokens, each of which the oracle computes exactly.
+"""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import head_latent_attention_13_amd as mla
+from oracle import absorbed as OA
+from oracle import expanded as OE
+from synthetic import Case, config, make_case, make_rows, make_x
+
+from .gpu_common import (DEV, assert_close, contiguous_cache, dev, dims_of, i32, paged_cache, run_step, tdtype,
+                         unpack, upload_weights)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    mla.load()
+
+
+@functools.lru_cache(maxsize=4)
+def case_of(idx, history="rows", batch=None, seed=None):
+    cfg = config(idx)
+    if batch is not None:
+        cfg = cfg.with_batch(batch)
+    return make_case(cfg, idx if seed is None else seed, history=history)
+
+
+def oracle_seq(case, b, rows_c=None, rows_k=None, **kw):
+    cfg = case.cfg
+    if rows_c is None:
+        S = int(case.cached[b])
+        if case.rows is not None:
+            rows_c, rows_k = case.rows[b][:, :cfg.d_latent], case.rows[b][:, cfg.d_latent:]
+        else:
+            rows_c, rows_k = OE.latent_rows(case.weights, case.x_hist[b], np.arange(S), cfg.rope_base)
+    return OE.decode_step(case.weights, cfg.rope_base, cfg.softmax_scale, case.x_new[b], int(case.cached[b]),
+                          rows_c, rows_k, **kw)
+
+
+def note(msg):
+    print(f"[gpu-step] {msg}", flush=True)
+
+
+# ------------------------------------------------------------- tiny fp32 ----
+def test_tiny_f32_end_to_end():
+    """Whole layer from token activations: history appended by the library."""
+    case = case_of(0, history="x")
+    cfg = case.cfg
+    S = int(case.cached[0])
+    note("tiny: absorb")
+    layer = mla.MLALayer(dims_of(cfg), upload_weights(case), max_batch=1, max_nq=max(S, 1))
+    cache, pool = contiguous_cache(cfg, [np.zeros((0, cfg.row), np.float32)], S + cfg.n_q)
+    note("tiny: append history")
+    layer.append(dev(case.x_hist[0], cfg), i32([0]), 1, S, cache)
+    note("tiny: decode step")
+    o_lat, lse, y = run_step(layer, cfg, case, cache)
+    ref = oracle_seq(case, 0)
+    assert_close(o_lat.cpu().numpy()[0], ref["o_lat"][0], cfg, "o_lat")
+    assert_close(lse.cpu().numpy()[0], ref["lse"][0], cfg, "lse")
+    assert_close(y.cpu().numpy()[0], ref["y"][0], cfg, "y")
+    # appended rows equal the oracle's latent rows
+    c_all, k_all = OE.latent_rows(case.weights, np.concatenate([case.x_hist[0], case.x_new[0]]),
+                                  np.arange(S + 1), cfg.rope_base)
+    rows = pool[0].cpu().numpy()
+    assert_close(rows[:, :cfg.d_latent], c_all, cfg, "appended latents")
+    assert_close(rows[:, cfg.d_latent:], k_all, cfg, "appended rope keys")
+    assert layer.device_error() == 0
+
+
+def test_tiny_f32_absorbed_weights():
+    case = case_of(0, history="x")
+    cfg = case.cfg
+    layer = mla.MLALayer(dims_of(cfg), upload_weights(case), max_batch=1)
+    offs, sizes, _ = mla.mla_absorbed_layout(layer.dims)
+    buf = layer.absorbed.cpu().numpy()
+    f = lambda i: buf[offs[i]:offs[i] + sizes[i]].view(np.float32)
+    uqk, uvo = OA.merged_weights(case.weights)
+    H, R, L = cfg.n_heads, cfg.row, cfg.d_latent
+    qc = unpack(f(2), cfg.d_q_latent, H * R, False).reshape(cfg.d_q_latent, H, R)
+    assert_close(qc[:, :, :L].transpose(1, 0, 2), uqk, cfg, "W_UQ W_UK^T")
+    assert_close(qc[:, :, L:], case.weights["W_QR"], cfg, "W_QR")
+    o = unpack(f(3), H * L, cfg.d_model, False).reshape(H, L, cfg.d_model)
+    assert_close(o, uvo, cfg, "W_UV W_O")
+    kv = unpack(f(0), cfg.d_model, R, False)
+    assert np.array_equal(kv[:, :L], case.weights["W_DKV"]) and np.array_equal(kv[:, L:], case.weights["W_KR"])
+
+
+# ----------------------------------------------------- V2 end-to-end slice ----
+def test_v2_end_to_end_from_activations():
+    """Two sequences of the V2 shape, 4096 history tokens each, appended by
+    the library from seeded activations, then one decode step."""
+    case = case_of(1, history="x", batch=2)
+    cfg = case.cfg
+    S = int(case.cached[0])
+    note("v2 e2e: absorb")
+    layer = mla.MLALayer(dims_of(cfg), upload_weights(case), max_batch=2, max_nq=S)
+    cache, pool = contiguous_cache(cfg, [np.zeros((0, cfg.row), np.float32)] * 2, S + 1)
+    note("v2 e2e: append history")
+    xh = dev(np.stack(case.x_hist).reshape(2 * S, cfg.d_model), cfg)
+    layer.append(xh, i32([0, 0]), 2, S, cache)
+    note("v2 e2e: decode step")
+    o_lat, lse, y = run_step(layer, cfg, case, cache)
+    for b in range(2):
+        ref = oracle_seq(case, b)
+        assert_close(o_lat.cpu().numpy()[b], ref["o_lat"][0], cfg, f"o_lat[b={b}]")
+        assert_close(lse.cpu().numpy()[b], ref["lse"][0], cfg, f"lse[b={b}]")
+        assert_close(y.cpu().numpy()[b], ref["y"][0], cfg, f"y[b={b}]")
+    # sampled appended rows against the oracle's fp64 rows
+    rows = pool[1].float().cpu().numpy()
+    pick = np.array([0, 1, 31, 32, 1000, 4095, 4096])
+    xs = np.concatenate([case.x_hist[1], case.x_new[1]])[pick]
+    c_ref, k_ref = OE.latent_rows(case.weights, xs, pick, cfg.rope_base)
+    assert_close(rows[pick, :cfg.d_latent], c_ref, cfg, "appended latents")
+    assert_close(rows[pick, cfg.d_latent:], k_ref, cfg, "appended rope keys")
+
+
+# ------------------------------------------------------ V2 contiguous B=16 ----
+def test_v2_decode_contiguous():
+    case = case_of(1)
+    cfg = case.cfg
+    note("v2 contiguous: absorb + cache")
+    layer = mla.MLALayer(dims_of(cfg), upload_weights(case), max_batch=cfg.batch)
+    cache, _ = contiguous_cache(cfg, case.rows, int(case.cached.max()) + 1)
+    note("v2 contiguous: decode step")
+    o_lat, lse, y = run_step(layer, cfg, case, cache)
+    for b in (0, 7, 15):
+        ref = oracle_seq(case, b)
+        assert_close(o_lat.cpu().numpy()[b], ref["o_lat"][0], cfg, f"o_lat[b={b}]")
+        assert_close(lse.cpu().numpy()[b], ref["lse"][0], cfg, f"lse[b={b}]")
+        assert_close(y.cpu().numpy()[b], ref["y"][0], cfg, f"y[b={b}]")
+    # a second identical call is bit-identical (no races in the LDS pipeline)
+    o2, l2, y2 = run_step(layer, cfg, case, cache, do_append=False)
+    assert torch.equal(o_lat, o2) and torch.equal(lse, l2) and torch.equal(y, y2)
+    assert layer.device_error() == 0
+
+
+# ------------------------------------------------------------ V2 paged ----
+def test_v2_decode_paged_and_bit_exact_gather():
+    case = case_of(2)
+    cfg = case.cfg
+    kv = case.cached + 1
+    note("v2 paged: absorb + caches")
+    layer = mla.MLALayer(dims_of(cfg), upload_weights(case), max_batch=cfg.batch)
+    cache, pool = paged_cache(cfg, case.rows, case.page_table, case.n_pages, kv)
+    note("v2 paged: decode step")
+    o_lat, lse, y = run_step(layer, cfg, case, cache)
+    order = np.argsort(case.cached)
+    for b in (int(order[0]), int(order[len(order) // 2]), int(order[-1])):
+        ref = oracle_seq(case, b)
+        assert_close(o_lat.cpu().numpy()[b], ref["o_lat"][0], cfg, f"o_lat[b={b}, len={kv[b]}]")
+        assert_close(y.cpu().numpy()[b], ref["y"][0], cfg, f"y[b={b}]")
+        assert_close(lse.cpu().numpy()[b], ref["lse"][0], cfg, f"lse[b={b}]")
+    # the same logical cache laid out contiguously gives bit-identical output
+    note("v2 paged: contiguous copy")
+    ccache, cpool = contiguous_cache(cfg, case.rows, int(kv.max()))
+    o_c, l_c, y_c = run_step(layer, cfg, case, ccache)
+    assert torch.equal(o_lat, o_c) and torch.equal(lse, l_c) and torch.equal(y, y_c)
+    # appended rows are byte-identical between the two layouts
+    P = cfg.page_size
+    tbl = case.page_table
+    for b in range(cfg.batch):
+        p = int(case.cached[b])
+        paged_row = pool[int(tbl[b, p // P]), p % P]
+        assert torch.equal(paged_row.view(torch.int16), cpool[b, p].view(torch.int16))
+    # NaN in every slot no sequence owns leaves the output unchanged
+    note("v2 paged: NaN-poisoned pool")
+    pcache, _ = paged_cache(cfg, case.rows, case.page_table, case.n_pages, kv, poison=True)
+    o_p, l_p, y_p = run_step(layer, cfg, case, pcache)
+    assert torch.equal(o_lat, o_p) and torch.equal(lse, l_p) and torch.equal(y, y_p)
+    assert layer.device_error() == 0
+
+
+# ------------------------------------------------------- V2 long context ----
+def test_v2_long_context_split_kv():
+    case = case_of(3)
+    cfg = case.cfg
+    kv = case.cached + 1
+    note("v2 long: absorb + cache")
+    layer = mla.MLALayer(dims_of(cfg), upload_weights(case), max_batch=cfg.batch)
+    cache, _ = paged_cache(cfg, case.rows, case.page_table, case.n_pages, kv)
+    note("v2 long: decode step")
+    o_lat, lse, y = run_step(layer, cfg, case, cache)
+    b = 2
+    heads = [0, 17, 64, 127]
+    ref = oracle_seq(case, b, heads=heads, want_y=False)
+    assert_close(o_lat.cpu().numpy()[b][heads], ref["o_lat"][0], cfg, "o_lat (sampled heads)")
+    assert_close(lse.cpu().numpy()[b][heads], ref["lse"][0], cfg, "lse (sampled heads)")
+    # y through the absorbed fp64 form (pinned to the expanded one on the CPU)
+    W = case.weights
+    uqk, uvo = OA.merged_weights(W)
+    S = int(case.cached[b])
+    c = np.concatenate([case.rows[b][:, :cfg.d_latent], ref["c_new"]])
+    k = np.concatenate([case.rows[b][:, cfg.d_latent:], ref["k_pe_new"]])
+    q_lat, q_pe = OA.query_latent(W, uqk, case.x_new[b], np.array([S]), cfg.rope_base)
+    ab = OA.attention(q_lat, q_pe, c, k, np.array([S]), cfg.softmax_scale, uvo)
+    assert_close(y.cpu().numpy()[b], ab["y"][0], cfg, "y")
+    assert_close(o_lat.cpu().numpy()[b], ab["o_lat"][0], cfg, "o_lat (all heads, absorbed oracle)")
+
+
+# ---------------------------------------------------- V3 chunked prefill ----
+def test_v3_chunked_prefill_causal():
+    case = case_of(4)
+    cfg = case.cfg
+    n_q = cfg.n_q
+    note("v3 prefill: absorb + cache")
+    layer = mla.MLALayer(dims_of(cfg), upload_weights(case), max_batch=cfg.batch, max_nq=n_q)
+    cache, _ = contiguous_cache(cfg, case.rows, int(case.cached.max()) + n_q)
+    note("v3 prefill: chunk step")
+    o_lat, lse, y = run_step(layer, cfg, case, cache)
+    o_lat = o_lat.view(cfg.batch, n_q, cfg.n_heads, cfg.d_latent)
+    lse = lse.view(cfg.batch, n_q, cfg.n_heads)
+    y = y.view(cfg.batch, n_q, cfg.d_model)
+    b = 1
+    S = int(case.cached[b])
+    js = np.array([0, 1, 511, 1023])
+    W = case.weights
+    xs = case.x_new[b]
+    c_new, k_new = OE.latent_rows(W, xs, S + np.arange(n_q), cfg.rope_base)
+    c = np.concatenate([case.rows[b][:, :cfg.d_latent], c_new])
+    k = np.concatenate([case.rows[b][:, cfg.d_latent:], k_new])
+    _, qn, qp = OE.query(W, xs[js], S + js, cfg.rope_base)
+    ref = OE.attention(W, qn, qp, c, k, S + js, cfg.softmax_scale)
+    assert_close(o_lat.cpu().numpy()[b][js], ref["o_lat"], cfg, "o_lat (sampled queries)")
+    assert_close(lse.cpu().numpy()[b][js], ref["lse"], cfg, "lse (sampled queries)")
+    assert_close(y.cpu().numpy()[b][js], ref["y"], cfg, "y (sampled queries)")
+
+
+# ------------------------------------------------------------ edge cases ----
+@pytest.mark.parametrize("lengths,n_q", [
+    ([0], 1),                 # first token: only itself visible
+    ([31, 32, 33, 63], 1),    # tile boundaries
+    ([1, 95, 200], 1),
+    ([0, 40], 5),             # causal inside a small chunk, from an empty cache
+    ([70], 33),               # chunk crossing tile boundaries
+])
+def test_edge_lengths(lengths, n_q):
+    cfg = config(1).with_(batch=len(lengths), cached=0, n_q=n_q, name=f"edge{lengths}x{n_q}")
+    rng = np.random.default_rng(1000 + 7 * len(lengths) + n_q)
+    cached = np.array(lengths, dtype=np.int64)
+    case = Case(cfg=cfg, seed=21, weights=case_of(1).weights, cached=cached,
+                x_new=make_x(cfg, (cfg.batch, n_q, cfg.d_model), rng), rows=make_rows(cfg, cached, rng))
+    note(f"edge {lengths} n_q={n_q}")
+    layer = mla.MLALayer(dims_of(cfg), upload_weights(case), max_batch=cfg.batch, max_nq=n_q)
+    cache, _ = contiguous_cache(cfg, case.rows, int(case.cached.max()) + n_q)
+    o_lat, lse, y = run_step(layer, cfg, case, cache)
+    o_lat = o_lat.view(cfg.batch, n_q, cfg.n_heads, cfg.d_latent).cpu().numpy()
+    y = y.view(cfg.batch, n_q, cfg.d_model).cpu().numpy()
+    for b in range(cfg.batch):
+        ref = oracle_seq(case, b)
+        assert_close(o_lat[b], ref["o_lat"], cfg, f"o_lat[b={b}]")
+        assert_close(y[b], ref["y"], cfg, f"y[b={b}]")
+    assert layer.device_error() == 0
+
+
+def test_device_errors_are_flagged_and_contained():
+    """A length beyond the cache poisons only its own sequence; a page id
+    outside the pool is flagged and never dereferenced."""
+    base = config(2)
+    cfg = base.with_(batch=4, cached=(100, 300), name="errors")
+    case = make_case(cfg, 5)
+    kv = case.cached + 1
+    layer = mla.MLALayer(dims_of(cfg), upload_weights(case), max_batch=cfg.batch)
+    cache, _ = paged_cache(cfg, case.rows, case.page_table, case.n_pages, kv)
+    x = dev(case.x_new.reshape(cfg.batch, cfg.d_model), cfg)
+    layer.append(x, i32(case.cached), cfg.batch, 1, cache)
+    bad_kv = kv.copy()
+    bad_kv[1] = case.page_table.shape[1] * cfg.page_size + 5
+    o_lat = torch.empty(cfg.batch, cfg.n_heads, cfg.d_latent, device=DEV)
+    note("errors: kv_len beyond capacity")
+    layer.decode(x, i32(bad_kv), cfg.batch, 1, cache, o_lat, None)
+    torch.cuda.synchronize()
+    assert layer.device_error() & 4
+    o = o_lat.cpu().numpy()
+    assert np.isnan(o[1]).all()
+    for b in (0, 2, 3):
+        assert_close(o[b], oracle_seq(case, b)["o_lat"][0], cfg, f"o_lat[b={b}] next to a bad sequence")
+    note("errors: page id outside the pool")
+    bad_table = case.page_table.copy()
+    bad_table[0, 0] = case.n_pages + 1000
+    bcache = mla.Cache(pool=cache.pool, page_table=i32(bad_table), page_size=cfg.page_size, n_pages=case.n_pages,
+                       max_pages_per_seq=bad_table.shape[1])
+    layer.decode(x, i32(kv), cfg.batch, 1, bcache, o_lat, None)
+    torch.cuda.synchronize()
+    assert layer.device_error() & 2
+    assert layer.device_error() == 0  # read clears

@@ -116,13 +116,11 @@ MUTATIONS = [
     # (module, old, new): each is a plausible slip in the oracle
     ("expanded", "(qp @ k_pe.T[None])", "(0.0 * (qp @ k_pe.T[None]))"),           # dropped RoPE term
     ("expanded", "<= q_pos[:, None]", "< q_pos[:, None] + 2"),                       # causal off by one
-    ("expanded", 'einsum("ml,lhd->hmd", c, W_UK[:, blk, :])',
-                 'einsum("ml,lhd->hmd", c, W_UV[:, blk, :])'),                         # wrong up-projection
+    ("expanded", "k_nope = (c @ W_UK[:, blk, :]", "k_nope = (c @ W_UV[:, blk, :]"),  # wrong up-projection
     ("expanded", "scores = scores * scale", "scores = scores * scale * scale"),      # wrong scale
-    ("expanded", 'einsum("hnd,hdm->nm", ob, W_O[blk])',
-                 'einsum("hnd,hdm->nm", ob, W_O[::-1][blk])'),                         # wrong head's W_O
-    ("expanded", 'np.einsum("nl,lhd->nhd", c_q, _f64(W["W_UQ"]))',
-                 'np.einsum("nl,lhd->nhd", c_q, _f64(W["W_UQ"])[:, ::-1])'),           # head index
+    ("expanded", "@ W_O[blk].reshape", "@ W_O[::-1][blk].reshape"),               # wrong head's W_O
+    ("expanded", "W_UQ, W_QR = _f64(W[\"W_UQ\"]), _f64(W[\"W_QR\"])",
+                 "W_UQ, W_QR = _f64(W[\"W_UQ\"])[:, ::-1], _f64(W[\"W_QR\"])"),          # head index
     ("expanded", "k_pe = _rope.apply(x @ _f64(W[\"W_KR\"]), np.asarray(pos), base)",
                  "k_pe = _rope.apply(x @ _f64(W[\"W_KR\"]), np.asarray(pos) + 1, base)"),  # key position
     ("expanded", "p = e / den ", "p = e / den.sum() "),                               # normalisation
