@@ -1,0 +1,276 @@
+#!/usr/bin/env python3
+"""MLA decode benchmark on one MI355X.
+
+A step is one pass of the layer's hot path over one batch, through the C
+ABI: mla_compress_append (latent down-projection + RoPE + append),
+mla_q_proj (merged query projection), mla_attention (split-KV attention over
+the latent cache + log-sum-exp merge) and mla_out_proj (merged output
+projection).  The default workload is the DeepSeek-V2-shaped decode layer:
+batch 16, 4096 cached tokens per sequence plus the new one, contiguous bf16
+latent cache, fp32 accumulation.  Inputs are seeded and synthetic and sit in
+HBM before the timed region starts.
+
+Prints ONE JSON line (see the "roofline" and "cpu_baseline" objects).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+F32_PEAK_TFLOPS = 157.3      # MI355X dense fp32 MFMA
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+KERNEL_SOURCES = ("mla_gemm.hip", "mla_attn.hip", "mla_common.h")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--config", type=int, default=1, help="workload index (1: V2 decode, B=16 x 4096)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget for the oracle sample")
+    p.add_argument("--copy-calib-mb", type=int, default=0,
+                   help="only run a plain device copy of this many MB (counter calibration)")
+    return p.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for s in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "head_latent_attention_13_amd", "csrc", s), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(call: str):
+    """HBM bytes per launch from the committed counter runs, if they were
+    taken on the current kernel sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    return t.get("calls", {}).get(call)
+
+
+def copy_calibration(mb: int, steps: int):
+    import torch
+    n = mb * (1 << 20) // 4
+    a = torch.ones(n, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n * 4, "launches": steps}))
+
+
+def cpu_baseline(case, n_budget_s: float):
+    """Oracle (expanded fp64) decode steps on a bounded sample of sequences."""
+    import numpy as np
+    import threadpoolctl
+    from oracle import expanded as OE
+    cfg = case.cfg
+    W = {k: np.asarray(v, np.float64) for k, v in case.weights.items()}
+    info = threadpoolctl.threadpool_info()
+    cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    done, t0 = 0, time.perf_counter()
+    for b in range(cfg.batch):
+        rows = case.rows[b]
+        OE.decode_step(W, cfg.rope_base, cfg.softmax_scale, case.x_new[b], int(case.cached[b]),
+                       rows[:, :cfg.d_latent], rows[:, cfg.d_latent:])
+        done += 1
+        if time.perf_counter() - t0 > n_budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done * cfg.n_q / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"expanded fp64 oracle decode step for {done} of {cfg.batch} sequences "
+                      f"({int(case.cached[0]) + cfg.n_q} visible rows each, all {cfg.n_heads} heads), "
+                      f"{dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (batch sharding would need no "
+              "exchange; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    if args.copy_calib_mb:
+        copy_calibration(args.copy_calib_mb, args.steps)
+        return
+
+    import head_latent_attention_13_amd as mla
+    from synthetic import config, make_case
+
+    torch.cuda.set_device(0)
+    cfg = config(args.config)
+    case = make_case(cfg, args.config, history="rows")
+    B, n_q, H, R = cfg.batch, cfg.n_q, cfg.n_heads, cfg.row
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    devt = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda().to(tdt)
+    dims = mla.make_dims(cfg.d_model, H, cfg.d_latent, cfg.d_q_latent, cfg.d_nope, cfg.d_rope, cfg.d_v,
+                         cfg.dtype, cfg.rope_base)
+    raw = {k: devt(v) for k, v in case.weights.items()}
+
+    # one-time absorption, timed on its own
+    torch.cuda.synchronize()
+    t_abs0 = torch.cuda.Event(enable_timing=True)
+    t_abs1 = torch.cuda.Event(enable_timing=True)
+    t_abs0.record()
+    layer = mla.MLALayer(dims, raw, max_batch=B, max_nq=n_q)
+    t_abs1.record()
+    torch.cuda.synchronize()
+    absorb_ms = t_abs0.elapsed_time(t_abs1)
+    del raw
+
+    kv_len = case.cached + n_q
+    if cfg.paged:
+        P = cfg.page_size
+        table = torch.from_numpy(case.page_table).cuda()
+        pool = torch.zeros(case.n_pages, P, R, dtype=tdt, device="cuda")
+        for b in range(B):
+            npg = (int(kv_len[b]) + P - 1) // P
+            tmp = torch.zeros(npg * P, R, dtype=tdt, device="cuda")
+            tmp[:len(case.rows[b])] = devt(case.rows[b])
+            pool[table[b, :npg].long()] = tmp.view(npg, P, R)
+        cache = mla.Cache(pool=pool, page_table=table, page_size=P, n_pages=case.n_pages,
+                          max_pages_per_seq=case.page_table.shape[1])
+    else:
+        s_max = int(kv_len.max())
+        pool = torch.zeros(B, s_max, R, dtype=tdt, device="cuda")
+        for b in range(B):
+            pool[b, :len(case.rows[b])] = devt(case.rows[b])
+        cache = mla.Cache(pool=pool, s_max=s_max)
+    x = devt(case.x_new.reshape(B * n_q, cfg.d_model))
+    pos = torch.from_numpy(case.cached.astype(np.int32)).cuda()
+    kv = torch.from_numpy(kv_len.astype(np.int32)).cuda()
+    q = torch.empty(B * n_q, H, R, dtype=tdt, device="cuda")
+    o_lat = torch.empty(B * n_q, H, cfg.d_latent, dtype=torch.float32, device="cuda")
+    y = torch.empty(B * n_q, cfg.d_model, dtype=torch.float32, device="cuda")
+
+    calls = ("mla_compress_append", "mla_q_proj", "mla_attention", "mla_out_proj")
+
+    def step(evs=None):
+        def mark(i):
+            if evs is not None:
+                evs[i].record()
+        mark(0)
+        layer.append(x, pos, B, n_q, cache)
+        mark(1)
+        layer.q_proj(x, kv, B, n_q, q)
+        mark(2)
+        layer.attention(q, kv, B, n_q, cache, o_lat)
+        mark(3)
+        layer.out_proj(o_lat, B * n_q, y)
+        mark(4)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for k in range(args.steps):
+        step(ev[k])
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    per_call_ms = {c: float(np.mean([ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(args.steps)]))
+                   for i, c in enumerate(calls)}
+    assert layer.device_error() == 0
+    ms_step = total_ms / args.steps
+
+    # ---- algorithmic bytes / flops per call (one step) ------------------
+    eb = 2 if cfg.dtype == "bf16" else 4
+    M = B * n_q
+    rows_visible = int(kv_len.sum())
+    pairs = int(sum(int(c) * n_q + n_q * (n_q + 1) // 2 for c in case.cached))  # unmasked (query, key) pairs
+    _, wbytes, _ = mla.mla_absorbed_layout(dims)
+    cache_bytes = (rows_visible if n_q == 1 else int(B * (int(case.cached.max()) + n_q))) * R * eb
+    algo = {
+        "mla_compress_append": {"bytes": wbytes[0] + M * cfg.d_model * eb + M * R * eb,
+                                "flops": 2 * M * cfg.d_model * R},
+        "mla_q_proj": {"bytes": wbytes[1] + wbytes[2] + M * cfg.d_model * eb + M * H * R * eb,
+                       "flops": 2 * M * cfg.d_model * cfg.d_q_latent + 2 * M * cfg.d_q_latent * H * R},
+        "mla_attention": {"bytes": cache_bytes + M * H * R * eb + M * H * cfg.d_latent * 4,
+                          "flops": 2 * H * pairs * (R + cfg.d_latent)},
+        "mla_out_proj": {"bytes": wbytes[3] + M * H * cfg.d_latent * 4 + M * cfg.d_model * 4,
+                         "flops": 2 * M * H * cfg.d_latent * cfg.d_model},
+    }
+    mfma_peak = BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else F32_PEAK_TFLOPS
+    kernels = {}
+    for c in calls:
+        t = per_call_ms[c] * 1e-3
+        gbs = algo[c]["bytes"] / t / 1e9
+        tfl = algo[c]["flops"] / t / 1e12
+        t_hbm = algo[c]["bytes"] / (HBM_PEAK_GBS * 1e9)
+        t_mfma = algo[c]["flops"] / (mfma_peak * 1e12)
+        bound = "hbm" if t_hbm >= t_mfma else "mfma"
+        kernels[c] = {"ms": round(per_call_ms[c], 4), "bound": bound, "GB_s": round(gbs, 1),
+                      "TFLOP_s": round(tfl, 2), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                      "mfma_frac": round(tfl / mfma_peak, 4),
+                      "roofline_frac": round((t_hbm if bound == "hbm" else t_mfma) / t, 4)}
+    dom = max(calls, key=lambda c: per_call_ms[c])
+    d = kernels[dom]
+    traffic = measured_traffic(dom)
+    if d["bound"] == "hbm":
+        roofline = {"bound": "hbm", "achieved": d["GB_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(d["GB_s"] / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom}
+    else:
+        roofline = {"bound": "mfma", "achieved": d["TFLOP_s"], "peak": mfma_peak, "unit": "TFLOP/s",
+                    "frac": round(d["TFLOP_s"] / mfma_peak, 4), "traffic": traffic, "kernel": dom}
+    att = kernels["mla_attention"]
+
+    out = {
+        "metric": "MLA decode tokens/s + latent-cache HBM GB/s & MFMA % of peak, 1 MI355X",
+        "value": round(M / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded; random-init weights of the DeepSeek-V2 layer shape)",
+        "config": {"workload": cfg.name, "batch": B, "cached_tokens": (list(cfg.cached) if isinstance(cfg.cached, tuple)
+                                                                      else int(cfg.cached)),
+                   "new_tokens": n_q, "heads": H, "d_latent": cfg.d_latent, "d_rope": cfg.d_rope,
+                   "d_model": cfg.d_model, "cache": "paged" if cfg.paged else "contiguous"},
+        "roofline": roofline,
+        "latent_cache_GB_s": round(cache_bytes / (per_call_ms["mla_attention"] * 1e-3) / 1e9, 1),
+        "attention_mfma_pct": round(100 * att["mfma_frac"], 2),
+        "attention_roofline_frac": att["roofline_frac"],
+        # measured from the allocation (paged pools round up to whole pages)
+        "kv_bytes_per_token_per_layer": round(pool.numel() * pool.element_size() / int(kv_len.sum()), 1),
+        "kernels": kernels,
+        "absorb_ms_once": round(absorb_ms, 3),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -119,6 +119,7 @@ WsLayout ws_layout(const mla_dims* d, int batch, int n_q) {
   W.cq = o; o = align256(o + (size_t)M * d->d_q_latent * esize(d));
   size_t part = std::max(std::max(W.g_app.part_bytes, W.g_cq.part_bytes), std::max(W.g_q.part_bytes, W.g_out.part_bytes));
   W.part = o; o = align256(o + part);
+
   const int HG = attn_head_group(bf);
   const size_t U = (size_t)M * ((H + HG - 1) / HG);
   W.tile_off = o; o = align256(o + (U + 1) * 4);
@@ -151,18 +152,19 @@ mla_status check_cache(const mla_dims* d, const mla_cache* c, int batch) {
   return MLA_OK;
 }
 
-mla_status run_gemm(const GemmPlan& g, bool bf16, bool a_f32, const void* A, int lda, const void* Wp, float* part,
-                    hipStream_t s) {
-  hipError_t e = launch_gemm(g, bf16, a_f32, A, lda, Wp, part, s);
-  if (e != hipSuccess) return hip_fail(e, "gemm launch");
+enum { G_APP = 0, G_CQ = 1, G_Q = 2, G_OUT = 3 };
+
+mla_status run_gemm(const WsLayout& W, int which, const GemmPlan& g, bool bf16, bool a_f32, const void* A, int lda,
+                    const void* Wp, unsigned char* ws, const EpiArgs& e, hipStream_t s) {
+  (void)which;
+  hipError_t err = launch_gemm(g, bf16, a_f32, A, lda, Wp, reinterpret_cast<float*>(ws + W.part), nullptr, e, s);
+  if (err != hipSuccess) return hip_fail(err, "gemm launch");
   return MLA_OK;
 }
 
-EpiArgs base_epi(const GemmPlan& g, int mode, const float* part, void* out) {
+EpiArgs base_epi(int mode, void* out) {
   EpiArgs e{};
   e.mode = mode;
-  e.M = g.M; e.N = g.N; e.Np = g.Np; e.ksplit = g.ksplit;
-  e.part = part;
   e.out = out;
   return e;
 }
@@ -171,22 +173,15 @@ mla_status q_proj_impl(const mla_dims* d, const WsLayout& W, const unsigned char
                        const int32_t* kv_len, int batch, int n_q, void* q, unsigned char* ws, hipStream_t s) {
   const bool bf = is_bf16(d);
   const AbsLayout L = abs_layout(d);
-  float* part = reinterpret_cast<float*>(ws + W.part);
   void* cq = ws + W.cq;
-  mla_status st = run_gemm(W.g_cq, bf, false, x, d->d_model, abs + L.off[1], part, s);
+  mla_status st = run_gemm(W, G_CQ, W.g_cq, bf, false, x, d->d_model, abs + L.off[1], ws, base_epi(EPI_STORE_T, cq), s);
   if (st) return st;
-  EpiArgs e = base_epi(W.g_cq, EPI_STORE_T, part, cq);
-  hipError_t he = launch_epilogue(e, bf, s);
-  if (he != hipSuccess) return hip_fail(he, "epilogue launch");
-  st = run_gemm(W.g_q, bf, false, cq, d->d_q_latent, abs + L.off[2], part, s);
-  if (st) return st;
-  e = base_epi(W.g_q, EPI_Q, part, q);
+  EpiArgs e = base_epi(EPI_Q, q);
   e.d_latent = d->d_latent; e.d_rope = d->d_rope; e.row = row_width(d); e.rope_base = d->rope_base;
   e.n_q = n_q; e.kv_len = kv_len;
-  he = launch_epilogue(e, bf, s);
-  if (he != hipSuccess) return hip_fail(he, "epilogue launch");
+  st = run_gemm(W, G_Q, W.g_q, bf, false, cq, d->d_q_latent, abs + L.off[2], ws, e, s);
   (void)batch;
-  return MLA_OK;
+  return st;
 }
 
 mla_status attention_impl(const mla_dims* d, const WsLayout& W, const void* q, const int32_t* kv_len, int batch,
@@ -318,19 +313,15 @@ mla_status mla_compress_append(const mla_dims* d, const void* absorbed, const vo
   const bool bf = is_bf16(d);
   const AbsLayout L = abs_layout(d);
   unsigned char* ws = reinterpret_cast<unsigned char*>(workspace);
-  float* part = reinterpret_cast<float*>(ws + W.part);
-  st = run_gemm(W.g_app, bf, false, x, d->d_model, reinterpret_cast<const unsigned char*>(absorbed) + L.off[0], part, s);
-  if (st) return st;
-  EpiArgs e = base_epi(W.g_app, EPI_APPEND, part, nullptr);
+  EpiArgs e = base_epi(EPI_APPEND, nullptr);
   e.d_latent = d->d_latent; e.d_rope = d->d_rope; e.row = row_width(d); e.rope_base = d->rope_base;
   e.n_q = n_q; e.pos = pos;
   e.pool = cache->pool; e.page_table = cache->page_table; e.paged = cache->page_table != nullptr;
   e.page_size = cache->page_size; e.n_pages = cache->n_pages; e.max_pages = cache->max_pages_per_seq;
   e.s_max = cache->s_max;
   e.err = reinterpret_cast<int32_t*>(ws + W.err);
-  hipError_t he = launch_epilogue(e, bf, s);
-  if (he != hipSuccess) return hip_fail(he, "append launch");
-  return MLA_OK;
+  return run_gemm(W, G_APP, W.g_app, bf, false, x, d->d_model, reinterpret_cast<const unsigned char*>(absorbed) + L.off[0],
+                  ws, e, s);
 }
 
 mla_status mla_q_proj(const mla_dims* d, const void* absorbed, const void* x, const int32_t* kv_len, int32_t batch,
@@ -391,14 +382,8 @@ mla_status mla_out_proj(const mla_dims* d, const void* absorbed, const float* o_
   const bool bf = is_bf16(d);
   const AbsLayout L = abs_layout(d);
   unsigned char* ws = reinterpret_cast<unsigned char*>(workspace);
-  float* part = reinterpret_cast<float*>(ws + W.part);
-  st = run_gemm(W.g_out, bf, true, o_lat, d->n_heads * d->d_latent, reinterpret_cast<const unsigned char*>(absorbed) + L.off[3],
-                part, s);
-  if (st) return st;
-  EpiArgs e = base_epi(W.g_out, EPI_F32, part, y);
-  hipError_t he = launch_epilogue(e, bf, s);
-  if (he != hipSuccess) return hip_fail(he, "epilogue launch");
-  return MLA_OK;
+  return run_gemm(W, G_OUT, W.g_out, bf, true, o_lat, d->n_heads * d->d_latent,
+                  reinterpret_cast<const unsigned char*>(absorbed) + L.off[3], ws, base_epi(EPI_F32, y), s);
 }
 
 }  // extern "C"

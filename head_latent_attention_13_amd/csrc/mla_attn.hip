@@ -91,12 +91,32 @@ using CfgF32 = AttnCfg<float, 16, 1, 32, 8, 3>;
 // more than this (log2 units); P stays <= 2^8, exact in bf16 and fp32.
 constexpr float kRescaleSlack = 8.0f;
 
+// 16-byte-chunk swizzle of a tile row: logical chunk c of row r sits at
+// chunk c ^ swz(r).  Rows 8g+j of the four lane groups of a transposed PV
+// read, and the 8 rows of one ds_read_b128 pass of the score phase, land in
+// distinct banks.
+__device__ inline int swz(int r) { return (r ^ ((r >> 3) << 1)) & 7; }
+
 template <class C>
 __device__ inline int lds_off(int r, int e) {
   const int byte = e * C::ES;
   int chunk = byte >> 4;
-  if constexpr (C::SWZ) chunk ^= (r & 7);
+  if constexpr (C::SWZ) chunk ^= swz(r);
   return r * C::ROW_BYTES + (chunk << 4) + (byte & 15);
+}
+
+// max / sum with the lanes 16 and 32 apart (gfx950 permlane swaps, no LDS)
+__device__ inline float max_xor16_32(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float sum_xor16_32(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __device__ inline void vm_wait_rt(int n) {
@@ -143,11 +163,150 @@ __device__ inline void issue_tile(const AttnArgs& a, unsigned char* stage, int b
     const int in = wave + inst * C::NW;
     const int p = in * 64 + lane;
     const int r = p / C::ROW_CHUNKS, s = p % C::ROW_CHUNKS;
-    const int c = C::SWZ ? (s ^ (r & 7)) : s;
+    const int c = C::SWZ ? (s ^ swz(r)) : s;
     const bool valid = ok && (t0 + r < vis);
     const void* src =
         valid ? (const void*)(gbase + r * C::ROW_BYTES + c * 16) : (const void*)(g_zero_rows + lane * 16);
     __builtin_amdgcn_global_load_lds(src, MLA_LDS_PTR(stage + in * 1024), 16, 0, 0);
+  }
+}
+
+// One 32-token tile of a segment: issue the DMA of a later tile into
+// `dma_stage`, then the score phase, online softmax and PV phase on `tb`.
+// The LDS pointers are restrict-qualified: within one call the stage being
+// filled, the stage being read and the P / alpha buffers never overlap, which
+// lets the compiler's wait insertion keep the DMA of later tiles in flight
+// (the DMA of this tile was waited for explicitly before the call).
+template <class C>
+__device__ __forceinline__ void tile_step(const AttnArgs& a, unsigned char* __restrict__ dma_stage,
+                                          const unsigned char* __restrict__ tb, typename C::T* __restrict__ p_s,
+                                          float* __restrict__ alpha_s, int* __restrict__ flag_s, bool issue,
+                                          int b, int k_issue, int tok0, int vis, int i, int wave, int lane,
+                                          const int (&s_base)[2][2], const int (&v_base)[4][2],
+                                          const typename C::F::frag (&qf)[C::HTW][C::RK], float (&m_run)[C::HTW],
+                                          float (&l_run)[C::HTW], f32x4 (&O)[C::NHT][C::NCT]) {
+  using T = typename C::T;
+  using F = typename C::F;
+  using frag = typename F::frag;
+  const int g = lane >> 4, l16 = lane & 15;
+  if (issue) issue_tile<C>(a, dma_stage, b, k_issue, vis, wave, lane);
+
+  // ---- S^T[32 tokens x 16 heads] = tile . q^T, per head tile ----------
+  // two accumulators per sub-tile (even / odd k-steps): four independent
+  // MFMA chains in flight
+  f32x4 sacc[C::HTW][2][2];
+#pragma unroll
+  for (int ht = 0; ht < C::HTW; ++ht)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) sacc[ht][u][0] = sacc[ht][u][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < C::RK; ++kb) {
+    frag a0, a1;
+    if constexpr (C::FAST) {
+      a0 = *reinterpret_cast<const frag*>(tb + s_base[0][kb & 1] + 128 * (kb >> 1));
+      a1 = *reinterpret_cast<const frag*>(tb + s_base[1][kb & 1] + 128 * (kb >> 1));
+    } else {
+      const int e = kb * C::KB + g * C::KPL;
+      a0 = *reinterpret_cast<const frag*>(tb + lds_off<C>(l16, e));
+      a1 = *reinterpret_cast<const frag*>(tb + lds_off<C>(16 + l16, e));
+    }
+#pragma unroll
+    for (int ht = 0; ht < C::HTW; ++ht) {
+      sacc[ht][0][kb & 1] = F::mma(a0, qf[ht][kb], sacc[ht][0][kb & 1]);
+      sacc[ht][1][kb & 1] = F::mma(a1, qf[ht][kb], sacc[ht][1][kb & 1]);
+    }
+  }
+
+  // ---- online softmax over this tile's 32 tokens, per head ------------
+  const bool tail = tok0 + C::TILE > vis;  // uniform: only the last tile is ragged
+#pragma unroll
+  for (int ht = 0; ht < C::HTW; ++ht) {
+    const int hl = (wave * C::HTW + ht) * 16 + l16;  // head within the group
+    float x[8];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      x[ii] = (sacc[ht][0][0][ii] + sacc[ht][0][1][ii]) * a.scale_log2;
+      x[4 + ii] = (sacc[ht][1][0][ii] + sacc[ht][1][1][ii]) * a.scale_log2;
+    }
+    if (tail) {
+      const int lim = vis - tok0 - 4 * g;
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        if (ii >= lim) x[ii] = -INFINITY;
+        if (16 + ii >= lim) x[4 + ii] = -INFINITY;
+      }
+    }
+    float mloc = x[0];
+#pragma unroll
+    for (int ii = 1; ii < 8; ++ii) mloc = fmaxf(mloc, x[ii]);
+    mloc = max_xor16_32(mloc);
+    const bool rebase = mloc > m_run[ht] + kRescaleSlack;
+    float alpha = 1.f;
+    if (rebase) {
+      alpha = __builtin_amdgcn_exp2f(m_run[ht] - mloc);
+      m_run[ht] = mloc;
+    }
+    float psum = 0.f, pv[8];
+#pragma unroll
+    for (int ii = 0; ii < 8; ++ii) {
+      pv[ii] = __builtin_amdgcn_exp2f(x[ii] - m_run[ht]);
+      psum += pv[ii];
+    }
+    psum = sum_xor16_32(psum);
+    l_run[ht] = l_run[ht] * alpha + psum;
+    T* prow = p_s + (size_t)hl * C::PSTR;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      prow[4 * g + ii] = from_f32<T>(pv[ii]);
+      prow[16 + 4 * g + ii] = from_f32<T>(pv[4 + ii]);
+    }
+    if (g == 0) alpha_s[hl] = alpha;
+    const bool any = __any(rebase);
+    if (lane == 0) flag_s[wave * C::HTW + ht] = any ? 1 : 0;
+  }
+  lds_barrier();
+
+  // ---- PV: O[group heads][this wave's columns] += P . tile ------------
+  if (i > 0) {
+#pragma unroll
+    for (int ht = 0; ht < C::NHT; ++ht) {
+      if (__builtin_amdgcn_readfirstlane(flag_s[ht])) {
+        const float4 a4 = *reinterpret_cast<const float4*>(alpha_s + ht * 16 + 4 * g);
+#pragma unroll
+        for (int ct = 0; ct < C::NCT; ++ct) {
+          O[ht][ct][0] *= a4.x;
+          O[ht][ct][1] *= a4.y;
+          O[ht][ct][2] *= a4.z;
+          O[ht][ct][3] *= a4.w;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int ks = 0; ks < C::PV_KS; ++ks) {
+    frag pa[C::NHT];
+#pragma unroll
+    for (int ht = 0; ht < C::NHT; ++ht)
+      pa[ht] = *reinterpret_cast<const frag*>(p_s + (size_t)(ht * 16 + l16) * C::PSTR + ks * C::KB + g * C::KPL);
+#pragma unroll
+    for (int ct = 0; ct < C::NCT; ++ct) {
+      frag bfr;
+      if constexpr (C::FAST) {
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+          bfr[jj] = *reinterpret_cast<const T*>(tb + v_base[(ct & 3) ^ (jj >> 1)][jj & 1] + jj * C::ROW_BYTES +
+                                                128 * (ct >> 2));
+      } else if constexpr (C::KPL == 1) {
+        bfr = *reinterpret_cast<const T*>(tb + lds_off<C>(ks * C::KB + g, wave * C::CPW + ct * 16 + l16));
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < C::KPL; ++jj)
+          bfr[jj] = *reinterpret_cast<const T*>(
+              tb + lds_off<C>(ks * C::KB + g * C::KPL + jj, wave * C::CPW + ct * 16 + l16));
+      }
+#pragma unroll
+      for (int ht = 0; ht < C::NHT; ++ht) O[ht][ct] = F::mma(pa[ht], bfr, O[ht][ct]);
+    }
   }
 }
 
@@ -177,13 +336,24 @@ __global__ __launch_bounds__(C::NTHR, 1) void attn_split_kernel(AttnArgs a) {
   T* p_s = reinterpret_cast<T*>(smem + C::OFF_P);
 
   // lane-constant LDS offsets (see the swizzle in issue_tile)
-  int s_base[2] = {0, 0}, v_base[2] = {0, 0};
+  // s_base[sub-tile][k-step parity]: row l16 (+16) reads logical chunk
+  // 4*kb + g; v_base[t][p]: rows 8g+j of the transposed PV read, with
+  // t = (ct & 3) ^ (j >> 1) and p = j & 1 (closed forms of lds_off)
+  int s_base[2][2] = {{0, 0}, {0, 0}}, v_base[4][2] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};
   if constexpr (C::FAST) {
-    const int x = l16 & 7, hb = l16 >> 3;
-    s_base[0] = l16 * C::ROW_BYTES + 16 * (g ^ x);
-    s_base[1] = l16 * C::ROW_BYTES + 16 * ((4 + g) ^ x);
-    v_base[0] = g * 8 * C::ROW_BYTES + 16 * wave * (C::CPW / 8) + 16 * hb + 2 * (l16 & 7);
-    v_base[1] = g * 8 * C::ROW_BYTES + 16 * wave * (C::CPW / 8) + 16 * (hb ^ 1) + 2 * (l16 & 7);
+    const int hb = l16 >> 3;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int r = l16 + 16 * sub;
+#pragma unroll
+      for (int par = 0; par < 2; ++par) s_base[sub][par] = r * C::ROW_BYTES + 16 * ((par * 4 + g) ^ swz(r));
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int par = 0; par < 2; ++par)
+        v_base[t][par] = g * 8 * C::ROW_BYTES + 16 * wave * (C::CPW / 8) + 16 * ((2 * (t ^ g) + (hb ^ par)) & 7) +
+                         2 * (l16 & 7);
   }
 
   // first stream holding tile g0
@@ -238,129 +408,10 @@ __global__ __launch_bounds__(C::NTHR, 1) void attn_split_kernel(AttnArgs a) {
       const int st = i % C::NSTAGE;
       vm_wait_rt(min(C::NSTAGE - 2, cnt - 1 - i) * n_loads);
       lds_barrier();
-      if (i + C::NSTAGE - 1 < cnt)
-        issue_tile<C>(a, smem + ((i + C::NSTAGE - 1) % C::NSTAGE) * C::TILE_BYTES, b, k0 + i + C::NSTAGE - 1, vis,
-                      wave, lane);
-      const unsigned char* tb = smem + st * C::TILE_BYTES;
-
-      // ---- S^T[32 tokens x 16 heads] = tile . q^T, per head tile --------
-      f32x4 sacc[C::HTW][2];
-#pragma unroll
-      for (int ht = 0; ht < C::HTW; ++ht) sacc[ht][0] = sacc[ht][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < C::RK; ++kb) {
-        frag a0, a1;
-        if constexpr (C::FAST) {
-          const int off = s_base[kb & 1] + 128 * (kb >> 1);
-          a0 = *reinterpret_cast<const frag*>(tb + off);
-          a1 = *reinterpret_cast<const frag*>(tb + off + 16 * C::ROW_BYTES);
-        } else {
-          const int e = kb * C::KB + g * C::KPL;
-          a0 = *reinterpret_cast<const frag*>(tb + lds_off<C>(l16, e));
-          a1 = *reinterpret_cast<const frag*>(tb + lds_off<C>(16 + l16, e));
-        }
-#pragma unroll
-        for (int ht = 0; ht < C::HTW; ++ht) {
-          sacc[ht][0] = F::mma(a0, qf[ht][kb], sacc[ht][0]);
-          sacc[ht][1] = F::mma(a1, qf[ht][kb], sacc[ht][1]);
-        }
-      }
-
-      // ---- online softmax over this tile's 32 tokens, per head ----------
-      const int tok0 = (k0 + i) * C::TILE;
-      const bool tail = tok0 + C::TILE > vis;  // uniform: only the last tile is ragged
-#pragma unroll
-      for (int ht = 0; ht < C::HTW; ++ht) {
-        const int hl = (wave * C::HTW + ht) * 16 + l16;  // head within the group
-        float x[8];
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          x[ii] = sacc[ht][0][ii] * a.scale_log2;
-          x[4 + ii] = sacc[ht][1][ii] * a.scale_log2;
-        }
-        if (tail) {
-          const int lim = vis - tok0 - 4 * g;
-#pragma unroll
-          for (int ii = 0; ii < 4; ++ii) {
-            if (ii >= lim) x[ii] = -INFINITY;
-            if (16 + ii >= lim) x[4 + ii] = -INFINITY;
-          }
-        }
-        float mloc = x[0];
-#pragma unroll
-        for (int ii = 1; ii < 8; ++ii) mloc = fmaxf(mloc, x[ii]);
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-        const bool rebase = mloc > m_run[ht] + kRescaleSlack;
-        float alpha = 1.f;
-        if (rebase) {
-          alpha = __builtin_amdgcn_exp2f(m_run[ht] - mloc);
-          m_run[ht] = mloc;
-        }
-        float psum = 0.f, pv[8];
-#pragma unroll
-        for (int ii = 0; ii < 8; ++ii) {
-          pv[ii] = __builtin_amdgcn_exp2f(x[ii] - m_run[ht]);
-          psum += pv[ii];
-        }
-        psum += __shfl_xor(psum, 16);
-        psum += __shfl_xor(psum, 32);
-        l_run[ht] = l_run[ht] * alpha + psum;
-        T* prow = p_s + (size_t)hl * C::PSTR;
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          prow[4 * g + ii] = from_f32<T>(pv[ii]);
-          prow[16 + 4 * g + ii] = from_f32<T>(pv[4 + ii]);
-        }
-        if (g == 0) alpha_s[hl] = alpha;
-        const bool any = __any(rebase);
-        if (lane == 0) flag_s[wave * C::HTW + ht] = any ? 1 : 0;
-      }
-      lds_barrier();
-
-      // ---- PV: O[group heads][this wave's columns] += P . tile ----------
-      if (i > 0) {
-#pragma unroll
-        for (int ht = 0; ht < C::NHT; ++ht) {
-          if (__builtin_amdgcn_readfirstlane(flag_s[ht])) {
-            const float4 a4 = *reinterpret_cast<const float4*>(alpha_s + ht * 16 + 4 * g);
-#pragma unroll
-            for (int ct = 0; ct < C::NCT; ++ct) {
-              O[ht][ct][0] *= a4.x;
-              O[ht][ct][1] *= a4.y;
-              O[ht][ct][2] *= a4.z;
-              O[ht][ct][3] *= a4.w;
-            }
-          }
-        }
-      }
-#pragma unroll
-      for (int ks = 0; ks < C::PV_KS; ++ks) {
-        frag pa[C::NHT];
-#pragma unroll
-        for (int ht = 0; ht < C::NHT; ++ht)
-          pa[ht] = *reinterpret_cast<const frag*>(p_s + (size_t)(ht * 16 + l16) * C::PSTR + ks * C::KB + g * C::KPL);
-#pragma unroll
-        for (int ct = 0; ct < C::NCT; ++ct) {
-          frag bfr;
-          if constexpr (C::FAST) {
-#pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-              const int off = v_base[jj & 1] + jj * C::ROW_BYTES + 128 * (ct >> 2) + 32 * ((ct & 3) ^ (jj >> 1));
-              bfr[jj] = *reinterpret_cast<const T*>(tb + off);
-            }
-          } else if constexpr (C::KPL == 1) {
-            bfr = *reinterpret_cast<const T*>(tb + lds_off<C>(ks * C::KB + g, wave * C::CPW + ct * 16 + l16));
-          } else {
-#pragma unroll
-            for (int jj = 0; jj < C::KPL; ++jj)
-              bfr[jj] = *reinterpret_cast<const T*>(
-                  tb + lds_off<C>(ks * C::KB + g * C::KPL + jj, wave * C::CPW + ct * 16 + l16));
-          }
-#pragma unroll
-          for (int ht = 0; ht < C::NHT; ++ht) O[ht][ct] = F::mma(pa[ht], bfr, O[ht][ct]);
-        }
-      }
+      const bool issue = i + C::NSTAGE - 1 < cnt;
+      tile_step<C>(a, smem + ((i + C::NSTAGE - 1) % C::NSTAGE) * C::TILE_BYTES, smem + st * C::TILE_BYTES, p_s,
+                   alpha_s, flag_s, issue, b, k0 + i + C::NSTAGE - 1, (k0 + i) * C::TILE, vis, i, wave, lane,
+                   s_base, v_base, qf, m_run, l_run, O);
     }
 
     // ---- finalise the segment ----------------------------------------
@@ -460,73 +511,60 @@ __global__ __launch_bounds__(1024) void attn_plan_kernel(const int32_t* __restri
 }
 
 // Log-sum-exp merge of the pieces of every stream that was cut by a
-// work-group boundary.  Block = (stream, 16 heads of its group), 256 threads.
+// work-group boundary: lse = log2 sum_s 2^lse_s, o = sum_s 2^(lse_s - lse) O_s.
+// Block = (stream, HPB heads of its group); each thread owns 4 columns.
 template <int HP, int DL>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
-  constexpr int MAXS = 64;
-  __shared__ float wts[16][MAXS];
-  __shared__ float lse_s[16];
+  constexpr int TPH = DL / 4;                      // threads per head
+  constexpr int HPB = 256 / TPH;                   // heads per block
+  constexpr int MAXS = 32;
+  __shared__ float wts[HPB][MAXS];
+  __shared__ float lse_s[HPB];
   const int u = blockIdx.x, tid = threadIdx.x;
   const int v = u / a.n_hg, hgrp = u - v * a.n_hg;
-  const int hl0 = blockIdx.y * 16;                 // first head (within the group) of this block
-  const int h0 = hgrp * HP + hl0;                  // first global head
+  const int r = tid / TPH;                         // head slot in the block
+  const int hl = blockIdx.y * HPB + r;             // head within the group
+  const int h = hgrp * HP + hl;                    // global head
+  const int c0 = (tid % TPH) * 4;
+  const bool active = (hl < HP) && (h < a.H);
   const int G = a.G;
   const int Ttot = a.tile_off[a.U];
   const int per = (Ttot + G - 1) / G;
   const int t0 = a.tile_off[u], t1 = a.tile_off[u + 1];
   if (t1 == t0) {  // invalid length: flagged by the plan kernel; poison the output
-    for (int i = tid; i < 16 * DL; i += 256) {
-      const int h = h0 + i / DL;
-      if (h < a.H) a.o_lat[((size_t)v * a.H + h) * DL + (i % DL)] = NAN;
+    if (active) {
+      *reinterpret_cast<float4*>(a.o_lat + ((size_t)v * a.H + h) * DL + c0) = make_float4(NAN, NAN, NAN, NAN);
+      if (a.lse && c0 == 0) a.lse[(size_t)v * a.H + h] = NAN;
     }
-    if (a.lse && tid < 16 && h0 + tid < a.H) a.lse[(size_t)v * a.H + h0 + tid] = NAN;
     return;
   }
   const int wf = t0 / per, wl = (t1 - 1) / per;
   if (wf == wl) return;  // written whole by the split kernel
   const int n = wl - wf + 1;
-  if (tid < 16) {
-    const int hl = hl0 + tid;
-    if (hgrp * HP + hl < a.H) {
-      float mx = -INFINITY;
-      for (int s = 0; s < n; ++s) mx = fmaxf(mx, a.part_lse[(size_t)(wf + s + u) * HP + hl]);
-      float sum = 0.f;
-      for (int s = 0; s < n; ++s) sum += exp2f(a.part_lse[(size_t)(wf + s + u) * HP + hl] - mx);
-      const float L = mx + log2f(sum);
-      lse_s[tid] = L;
-      for (int s = 0; s < n && s < MAXS; ++s) wts[tid][s] = exp2f(a.part_lse[(size_t)(wf + s + u) * HP + hl] - L);
-      if (a.lse) a.lse[(size_t)v * a.H + hgrp * HP + hl] = L * 0.69314718055994531f;
-    }
+  if (tid % TPH == 0 && active) {
+    const float* pl = a.part_lse + (size_t)(wf + u) * HP + hl;   // piece s at pl[s * HP]
+    float mx = -INFINITY;
+    for (int s = 0; s < n; ++s) mx = fmaxf(mx, pl[(size_t)s * HP]);
+    float sum = 0.f;
+    for (int s = 0; s < n; ++s) sum += exp2f(pl[(size_t)s * HP] - mx);
+    const float L = mx + log2f(sum);
+    lse_s[r] = L;
+    for (int s = 0; s < n && s < MAXS; ++s) wts[r][s] = exp2f(pl[(size_t)s * HP] - L);
+    if (a.lse) a.lse[(size_t)v * a.H + h] = L * 0.69314718055994531f;
   }
   __syncthreads();
-  const int r = tid >> 4;  // head within the block
-  const int hl = hl0 + r;
-  if (hgrp * HP + hl >= a.H) return;
-  constexpr int PER_T = DL / 16;  // columns per thread
-  const int c0 = (tid & 15) * PER_T;
-  float acc[PER_T];
-#pragma unroll
-  for (int c = 0; c < PER_T; ++c) acc[c] = 0.f;
+  if (!active) return;
+  const float* src = a.part_o + ((size_t)(wf + u) * HP + hl) * DL + c0;  // piece s at src[s * HP * DL]
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int s = 0; s < n; ++s) {
     const float wgt = (s < MAXS) ? wts[r][s] : exp2f(a.part_lse[(size_t)(wf + s + u) * HP + hl] - lse_s[r]);
-    const float* src = a.part_o + ((size_t)(wf + s + u) * HP + hl) * DL + c0;
-    if constexpr (PER_T % 4 == 0) {
-#pragma unroll
-      for (int c = 0; c < PER_T; c += 4) {
-        const float4 x = *reinterpret_cast<const float4*>(src + c);
-        acc[c] += wgt * x.x;
-        acc[c + 1] += wgt * x.y;
-        acc[c + 2] += wgt * x.z;
-        acc[c + 3] += wgt * x.w;
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < PER_T; ++c) acc[c] += wgt * src[c];
-    }
+    const float4 x = *reinterpret_cast<const float4*>(src + (size_t)s * HP * DL);
+    acc.x += wgt * x.x;
+    acc.y += wgt * x.y;
+    acc.z += wgt * x.z;
+    acc.w += wgt * x.w;
   }
-  float* dst = a.o_lat + ((size_t)v * a.H + hgrp * HP + hl) * DL + c0;
-#pragma unroll
-  for (int c = 0; c < PER_T; ++c) dst[c] = acc[c];
+  *reinterpret_cast<float4*>(a.o_lat + ((size_t)v * a.H + h) * DL + c0) = acc;
 }
 
 int attn_supported(bool bf16, int H, int d_latent, int d_rope) {
@@ -555,7 +593,8 @@ static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(attn_split_kernel<C>, dim3(a.G), dim3(C::NTHR), C::LDS_BYTES, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_merge_kernel<C::HP, C::DL>), dim3(a.U, C::HP / 16), dim3(256), 0, s, a);
+  constexpr int hpb = 256 / (C::DL / 4);
+  hipLaunchKernelGGL((attn_merge_kernel<C::HP, C::DL>), dim3(a.U, (C::HP + hpb - 1) / hpb), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

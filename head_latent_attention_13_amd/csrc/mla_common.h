@@ -82,15 +82,18 @@ __device__ inline T from_f32(float v) { return (T)v; }
 // Packed ("fragment-ordered") weight layout used by every streamed weight.
 //
 // A logical row-major matrix W[K][N] (y = x W) is stored as
-//   [ceil(N/16)][Kp/KB][64 lanes][KPL]        Kp = roundup(K, KB)
+//   [Kp/KB][ceil(N/16)][64 lanes][KPL]       Kp = roundup(K, KB)
 // so that the B-operand fragment of one MFMA (16 columns x KB rows) is one
 // contiguous 64*KPL-element block: lane l holds W[kb*KB + (l/16)*KPL + j]
-// [nt*16 + l%16].  Padding (rows >= K, columns >= N) is zero.
+// [nt*16 + l%16].  Fragments are k-block-major: the fragments of adjacent
+// column tiles at one k-block are adjacent, so a wave that owns NT
+// neighbouring tiles reads one contiguous NT-fragment run per k-block.
+// Padding (rows >= K, columns >= N) is zero.
 // ------------------------------------------------------------------------
-__host__ __device__ inline size_t packed_index(int k, int n, int Kp, int KB, int KPL) {
+__host__ __device__ inline size_t packed_index(int k, int n, int Np, int KB, int KPL) {
   const int nt = n >> 4, kb = k / KB, kk = k - kb * KB;
   const int lane = (n & 15) + 16 * (kk / KPL), j = kk % KPL;
-  return ((size_t)nt * (size_t)(Kp / KB) + (size_t)kb) * (size_t)(64 * KPL) + (size_t)(lane * KPL + j);
+  return ((size_t)kb * (size_t)(Np / 16) + (size_t)nt) * (size_t)(64 * KPL) + (size_t)(lane * KPL + j);
 }
 
 // Wait until at most N vector-memory operations of this wave are in flight.

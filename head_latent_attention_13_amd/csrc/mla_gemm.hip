@@ -14,168 +14,20 @@
 namespace mla {
 
 // --------------------------------------------------------------------------
-// GEMM: part[ks][m][n] = sum_{k in slice ks} A[m][k] * W[k][n]
-// Block = 4 waves; wave -> one n-group (NT tiles of 16 columns), all MT
-// m-tiles of the block's m-group, one K slice.
-// --------------------------------------------------------------------------
-template <typename T, typename TA, int MT, int NT>
-__global__ __launch_bounds__(256) void gemm_stream_kernel(
-    const TA* __restrict__ A, int lda, int M, const T* __restrict__ Wp, int kblocks, int ntiles,
-    int kb_per_split, float* __restrict__ part, int Np) {
-  using F = Mfma<T>;
-  constexpr int KB = F::KB, KPL = F::KPL, FR = 64 * KPL;
-  const int lane = threadIdx.x & 63;
-  const int ng = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int nt0 = ng * NT;
-  if (nt0 >= ntiles) return;
-  const int mt0 = blockIdx.y * MT;
-  const int ks = blockIdx.z;
-  const int kb0 = ks * kb_per_split;
-  const int kb1 = min(kb0 + kb_per_split, kblocks);
-
-  f32x4 acc[MT][NT];
-#pragma unroll
-  for (int mi = 0; mi < MT; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < NT; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const TA* ap[MT];
-  bool aval[MT];
-#pragma unroll
-  for (int mi = 0; mi < MT; ++mi) {
-    const int m = (mt0 + mi) * 16 + (lane & 15);
-    aval[mi] = m < M;
-    ap[mi] = A + (size_t)(aval[mi] ? m : 0) * (size_t)lda + (lane >> 4) * KPL;
-  }
-  const T* wp[NT];
-#pragma unroll
-  for (int ni = 0; ni < NT; ++ni) {
-    const int nt = min(nt0 + ni, ntiles - 1);
-    wp[ni] = Wp + (size_t)nt * (size_t)kblocks * FR + lane * KPL;
-  }
-
-#pragma unroll 2
-  for (int kb = kb0; kb < kb1; ++kb) {
-    typename F::frag b[NT];
-#pragma unroll
-    for (int ni = 0; ni < NT; ++ni) b[ni] = load_frag<T>(wp[ni] + (size_t)kb * FR);
-    typename F::frag a[MT];
-#pragma unroll
-    for (int mi = 0; mi < MT; ++mi) {
-      if constexpr (sizeof(TA) == sizeof(T)) {
-        a[mi] = load_frag<T>(reinterpret_cast<const T*>(ap[mi]) + kb * KB);
-      } else {
-        a[mi] = load_frag_from_f32<T>(reinterpret_cast<const float*>(ap[mi]) + kb * KB);
-      }
-      if (!aval[mi]) a[mi] = F::zero();
-    }
-#pragma unroll
-    for (int mi = 0; mi < MT; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < NT; ++ni) acc[mi][ni] = F::mma(a[mi], b[ni], acc[mi][ni]);
-  }
-
-#pragma unroll
-  for (int mi = 0; mi < MT; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < NT; ++ni) {
-      const int nt = nt0 + ni;
-      if (nt >= ntiles) continue;
-      const int n = nt * 16 + (lane & 15);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = (mt0 + mi) * 16 + 4 * (lane >> 4) + i;
-        if (m < M) part[((size_t)ks * M + m) * Np + n] = acc[mi][ni][i];
-      }
-    }
-}
-
-static int ceil_div(int a, int b) { return (a + b - 1) / b; }
-
-GemmPlan plan_gemm(int M, int K, int N, bool bf16, int n_cu) {
-  GemmPlan g{};
-  g.M = M; g.K = K; g.N = N;
-  g.KB = bf16 ? Mfma<__bf16>::KB : Mfma<float>::KB;
-  g.Kp = ceil_div(K, g.KB) * g.KB;
-  g.Np = ceil_div(N, 16) * 16;
-  g.kblocks = g.Kp / g.KB;
-  g.ntiles = g.Np / 16;
-  g.NT = g.ntiles >= 64 ? 8 : 2;
-  const int mtiles = ceil_div(std::max(M, 1), 16);
-  g.MT = mtiles >= 4 ? 4 : (mtiles >= 2 ? 2 : 1);
-  g.ngroups = ceil_div(g.ntiles, g.NT);
-  g.mgroups = ceil_div(mtiles, g.MT);
-  // Enough waves to keep every SIMD streaming (about 8 per CU), but keep
-  // each K slice at least 16 blocks long so partial sums stay small.
-  const long target = (long)n_cu * 8;
-  const long base = (long)g.ngroups * g.mgroups;
-  int ks = (int)std::max(1L, target / std::max(base, 1L));
-  ks = std::min(ks, std::max(1, g.kblocks / 16));
-  g.kb_per_split = ceil_div(g.kblocks, ks);
-  g.ksplit = ceil_div(g.kblocks, g.kb_per_split);
-  g.part_bytes = (size_t)g.ksplit * (size_t)M * (size_t)g.Np * sizeof(float);
-  return g;
-}
-
-template <typename T, typename TA, int MT, int NT>
-static hipError_t launch_gemm_t(const GemmPlan& g, const void* A, int lda, const void* Wp, float* part,
-                                hipStream_t s) {
-  dim3 grid(ceil_div(g.ngroups, 4), g.mgroups, g.ksplit);
-  hipLaunchKernelGGL((gemm_stream_kernel<T, TA, MT, NT>), grid, dim3(256), 0, s,
-                     reinterpret_cast<const TA*>(A), lda, g.M, reinterpret_cast<const T*>(Wp), g.kblocks,
-                     g.ntiles, g.kb_per_split, part, g.Np);
-  return hipGetLastError();
-}
-
-template <typename T, typename TA>
-static hipError_t launch_gemm_mt(const GemmPlan& g, const void* A, int lda, const void* Wp, float* part,
-                                 hipStream_t s) {
-  if (g.NT == 8) {
-    switch (g.MT) {
-      case 1: return launch_gemm_t<T, TA, 1, 8>(g, A, lda, Wp, part, s);
-      case 2: return launch_gemm_t<T, TA, 2, 8>(g, A, lda, Wp, part, s);
-      default: return launch_gemm_t<T, TA, 4, 8>(g, A, lda, Wp, part, s);
-    }
-  }
-  switch (g.MT) {
-    case 1: return launch_gemm_t<T, TA, 1, 2>(g, A, lda, Wp, part, s);
-    case 2: return launch_gemm_t<T, TA, 2, 2>(g, A, lda, Wp, part, s);
-    default: return launch_gemm_t<T, TA, 4, 2>(g, A, lda, Wp, part, s);
-  }
-}
-
-hipError_t launch_gemm(const GemmPlan& g, bool bf16, bool a_f32, const void* A, int lda, const void* Wp,
-                       float* part, hipStream_t s) {
-  if (bf16) {
-    return a_f32 ? launch_gemm_mt<__bf16, float>(g, A, lda, Wp, part, s)
-                 : launch_gemm_mt<__bf16, __bf16>(g, A, lda, Wp, part, s);
-  }
-  return launch_gemm_mt<float, float>(g, A, lda, Wp, part, s);
-}
-
-// --------------------------------------------------------------------------
-// Epilogue: sum the K slices, then store / rotate / append.
-// One thread per column pair (n, n+1) so a RoPE pair is handled in-thread.
+// Epilogue of one column pair (n, n+1) of output row m, given final sums.
+// Pairs keep a RoPE rotation (pairs (2j, 2j+1) of the rope part) in-thread.
 // --------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(256) void epilogue_kernel(EpiArgs e) {
-  const int pairs = e.Np / 2;
-  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (long)e.M * pairs) return;
-  const int m = (int)(idx / pairs);
-  const int n = (int)(idx % pairs) * 2;
-  if (n >= e.N) return;
-  float v0 = 0.f, v1 = 0.f;
-  for (int ks = 0; ks < e.ksplit; ++ks) {
-    const float2 p = *reinterpret_cast<const float2*>(e.part + ((size_t)ks * e.M + m) * e.Np + n);
-    v0 += p.x;
-    v1 += p.y;
-  }
+__device__ inline void epi_pair(const EpiArgs& e, int m, int n, float v0, float v1) {
+  if (m >= e.M || n >= e.N) return;
   const bool has1 = n + 1 < e.N;
   if (e.mode == EPI_F32) {
     float* y = reinterpret_cast<float*>(e.out) + (size_t)m * e.N + n;
-    y[0] = v0;
-    if (has1) y[1] = v1;
+    if (has1) {
+      *reinterpret_cast<float2*>(y) = make_float2(v0, v1);
+    } else {
+      y[0] = v0;
+    }
     return;
   }
   if (e.mode == EPI_STORE_T) {
@@ -186,12 +38,7 @@ __global__ __launch_bounds__(256) void epilogue_kernel(EpiArgs e) {
   }
   const int b = m / e.n_q, t = m - b * e.n_q;
   const int f = n % e.row;  // column within one head's (latent | rope) row
-  int pos;
-  if (e.mode == EPI_Q) {
-    pos = e.kv_len[b] - e.n_q + t;
-  } else {
-    pos = e.pos[b] + t;
-  }
+  const int pos = (e.mode == EPI_Q) ? e.kv_len[b] - e.n_q + t : e.pos[b] + t;
   if (f >= e.d_latent) {
     float c, s;
     rope_cos_sin(pos, (f - e.d_latent) >> 1, e.d_rope, e.rope_base, &c, &s);
@@ -230,14 +77,269 @@ __global__ __launch_bounds__(256) void epilogue_kernel(EpiArgs e) {
   dst[n + 1] = from_f32<T>(v1);
 }
 
-hipError_t launch_epilogue(const EpiArgs& e, bool bf16, hipStream_t s) {
-  const long total = (long)e.M * (e.Np / 2);
-  const int blocks = (int)((total + 255) / 256);
-  if (bf16)
-    hipLaunchKernelGGL(epilogue_kernel<__bf16>, dim3(blocks), dim3(256), 0, s, e);
-  else
-    hipLaunchKernelGGL(epilogue_kernel<float>, dim3(blocks), dim3(256), 0, s, e);
+struct GemmArgs {
+  const void* A;
+  int lda;
+  const void* Wp;
+  int kblocks, ntiles, Np, ksplit, kb_per_split;
+  float* part;
+  EpiArgs e;
+};
+
+// --------------------------------------------------------------------------
+// Streamed-weight GEMM with the epilogue fused when the K range is not split
+// (see mla_internal.h).  With ksplit > 1 the block writes its fp32 slice of
+// the tile and splitk_epilogue_kernel finishes the sum in a second launch
+// (no cross-work-group fences: the kernel boundary orders the slices).
+// --------------------------------------------------------------------------
+template <typename T, typename TA, int MT, int NT, int KSW>
+__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
+  using F = Mfma<T>;
+  using frag = typename F::frag;
+  constexpr int KB = F::KB, KPL = F::KPL, FR = 64 * KPL;
+  constexpr int NGW = 4 / KSW;                 // column groups per block
+  constexpr int ROWS = MT * 16, COLS = NGW * NT * 16;
+  __shared__ float red[KSW][ROWS][COLS];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int M = g.e.M;
+  const int col0 = blockIdx.x * COLS;                                  // first column of the block tile
+  const int nt0 = blockIdx.x * NGW * NT + (KSW == 1 ? wave * NT : 0);
+  const int mt0 = blockIdx.y * MT;
+  const int ks = blockIdx.z;
+  int kb0 = ks * g.kb_per_split;
+  int kb1 = min(kb0 + g.kb_per_split, g.kblocks);
+  if (KSW > 1) {  // this wave's share of the slice
+    const int len = kb1 - kb0, per = (len + KSW - 1) / KSW;
+    kb0 = min(kb0 + wave * per, kb1);
+    kb1 = min(kb0 + per, kb1);
+  }
+
+  f32x4 acc[MT][NT];
+#pragma unroll
+  for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NT; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const TA* ap[MT];
+  bool aval[MT];
+#pragma unroll
+  for (int mi = 0; mi < MT; ++mi) {
+    const int m = (mt0 + mi) * 16 + (lane & 15);
+    aval[mi] = m < M;
+    ap[mi] = reinterpret_cast<const TA*>(g.A) + (size_t)(aval[mi] ? m : 0) * (size_t)g.lda + (lane >> 4) * KPL;
+  }
+  // k-block-major packed weights: tile nt at k-block kb is fragment kb*ntiles + nt
+  const size_t kb_stride = (size_t)g.ntiles * FR;
+  const T* wp[NT];
+#pragma unroll
+  for (int ni = 0; ni < NT; ++ni) {
+    const int nt = min(nt0 + ni, g.ntiles - 1);
+    wp[ni] = reinterpret_cast<const T*>(g.Wp) + (size_t)nt * FR + lane * KPL;
+  }
+
+  auto load_b = [&](frag (&b)[NT], int kb) {
+#pragma unroll
+    for (int ni = 0; ni < NT; ++ni) b[ni] = *reinterpret_cast<const frag*>(wp[ni] + (size_t)kb * kb_stride);
+  };
+  auto load_a = [&](frag (&a)[MT], int kb) {
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi) {
+      if constexpr (sizeof(TA) == sizeof(T)) {
+        a[mi] = load_frag<T>(reinterpret_cast<const T*>(ap[mi]) + kb * KB);
+      } else {
+        a[mi] = load_frag_from_f32<T>(reinterpret_cast<const float*>(ap[mi]) + kb * KB);
+      }
+      if (!aval[mi]) a[mi] = F::zero();
+    }
+  };
+  auto mma_all = [&](const frag (&a)[MT], const frag (&b)[NT]) {
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NT; ++ni) acc[mi][ni] = F::mma(a[mi], b[ni], acc[mi][ni]);
+  };
+  // U k-blocks per step: all their loads are issued before the first MFMA
+  constexpr int U = (32 / NT) > 1 ? (32 / NT) : 1;
+  int kb = kb0;
+  for (; kb + U <= kb1; kb += U) {
+    frag b[U][NT], a[U][MT];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      load_b(b[u], kb + u);
+      load_a(a[u], kb + u);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) mma_all(a[u], b[u]);
+  }
+  for (; kb < kb1; ++kb) {
+    frag b[NT], a[MT];
+    load_b(b, kb);
+    load_a(a, kb);
+    mma_all(a, b);
+  }
+
+  // ---- combine the block tile in LDS -----------------------------------
+  {
+    const int slot = KSW > 1 ? wave : 0;
+    const int cbase = KSW > 1 ? 0 : wave * NT * 16;
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NT; ++ni)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          red[slot][mi * 16 + 4 * (lane >> 4) + i][cbase + ni * 16 + (lane & 15)] = acc[mi][ni][i];
+  }
+  __syncthreads();
+  constexpr int PAIRS = ROWS * COLS / 2;
+  const int row0 = mt0 * 16;
+  for (int p = threadIdx.x; p < PAIRS; p += 256) {
+    const int r = p / (COLS / 2), c = (p % (COLS / 2)) * 2;
+    const int m = row0 + r, n = col0 + c;
+    if (m >= M || n >= g.Np) continue;
+    float v0 = 0.f, v1 = 0.f;
+#pragma unroll
+    for (int s2 = 0; s2 < KSW; ++s2) {
+      v0 += red[s2][r][c];
+      v1 += red[s2][r][c + 1];
+    }
+    if (g.ksplit == 1) {
+      epi_pair<T>(g.e, m, n, v0, v1);
+    } else {
+      *reinterpret_cast<float2*>(g.part + ((size_t)ks * M + m) * g.Np + n) = make_float2(v0, v1);
+    }
+  }
+}
+
+// Sum of the K slices in slice order (deterministic), then the epilogue.
+template <typename T>
+__global__ __launch_bounds__(256) void splitk_epilogue_kernel(GemmArgs g) {
+  const int pairs = g.Np / 2;
+  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (long)g.e.M * pairs) return;
+  const int m = (int)(idx / pairs);
+  const int n = (int)(idx % pairs) * 2;
+  float v0 = 0.f, v1 = 0.f;
+  for (int ks = 0; ks < g.ksplit; ++ks) {
+    const float2 p = *reinterpret_cast<const float2*>(g.part + ((size_t)ks * g.e.M + m) * g.Np + n);
+    v0 += p.x;
+    v1 += p.y;
+  }
+  epi_pair<T>(g.e, m, n, v0, v1);
+}
+
+static int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Column-tile counts per wave instantiated for the decode path.
+static const int kDecodeNT[] = {2, 4, 5, 8, 9, 10, 16};
+
+GemmPlan plan_gemm(int M, int K, int N, bool bf16, int n_cu) {
+  GemmPlan g{};
+  g.M = M; g.K = K; g.N = N;
+  g.KB = bf16 ? Mfma<__bf16>::KB : Mfma<float>::KB;
+  g.Kp = ceil_div(K, g.KB) * g.KB;
+  g.Np = ceil_div(N, 16) * 16;
+  g.kblocks = g.Kp / g.KB;
+  g.ntiles = g.Np / 16;
+  const int mtiles = ceil_div(std::max(M, 1), 16);
+  // Cost model for a weight-streaming kernel (units: 1 KB fragments): the
+  // busiest CU streams ceil(blocks / CUs) blocks of cols * kb_per_split
+  // fragments; fewer than two blocks per CU leave too few loads in flight;
+  // every K slice beyond the first adds an fp32 partial round trip and a
+  // second launch.
+  double best = 1e300;
+  long best_blocks = 0;
+  auto consider = [&](int MT, int NT, int KSW) {
+    const int cols = (4 / KSW) * NT;
+    const int gx = ceil_div(g.ntiles, cols), gy = ceil_div(mtiles, MT);
+    const int ksmax = std::max(1, g.kblocks / (2 * KSW));
+    for (int ks = 1; ks <= ksmax; ++ks) {
+      const int kbs = ceil_div(g.kblocks, ks);
+      if (ceil_div(g.kblocks, kbs) != ks) continue;
+      const long blocks = (long)gx * gy * ks;
+      double cost = (double)((blocks + n_cu - 1) / n_cu) * cols * kbs;
+      if (blocks < n_cu) cost *= 1.6;
+      else if (blocks < 2L * n_cu) cost *= 1.25;
+      if (ks > 1) cost += 2.0 * ks * M * g.Np * 4.0 / 1024.0 / n_cu + 100.0;
+      if (cost < best * 0.999 || (cost <= best * 1.001 && blocks < best_blocks)) {
+        best = cost;
+        best_blocks = blocks;
+        g.MT = MT; g.NT = NT; g.KSW = KSW; g.gx = gx; g.gy = gy; g.ksplit = ks; g.kb_per_split = kbs;
+      }
+    }
+  };
+  if (mtiles <= 4) {
+    // up to 64 rows: the block's waves split K; the LDS tile (4 x rows x
+    // cols fp32) stays within 64 KB
+    const int MT = mtiles == 1 ? 1 : (mtiles == 2 ? 2 : 4);
+    for (int nt : kDecodeNT)
+      if (MT * nt <= 16) consider(MT, nt, 4);
+  } else {
+    consider(4, 4, 1);
+  }
+  g.part_bytes = g.ksplit > 1 ? (size_t)g.ksplit * (size_t)M * (size_t)g.Np * sizeof(float) : 0;
+  g.counters = 0;
+  return g;
+}
+
+template <typename T, typename TA, int MT, int NT, int KSW>
+static hipError_t launch_gemm_t(const GemmPlan& g, const GemmArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((gemm_kernel<T, TA, MT, NT, KSW>), dim3(g.gx, g.gy, g.ksplit), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || g.ksplit == 1) return e;
+  const long total = (long)g.M * (g.Np / 2);
+  hipLaunchKernelGGL(splitk_epilogue_kernel<T>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);
   return hipGetLastError();
+}
+
+template <typename T, typename TA>
+static hipError_t launch_gemm_sel(const GemmPlan& g, const GemmArgs& a, hipStream_t s) {
+  if (g.KSW == 4 && g.MT == 1) {
+    switch (g.NT) {
+      case 2: return launch_gemm_t<T, TA, 1, 2, 4>(g, a, s);
+      case 4: return launch_gemm_t<T, TA, 1, 4, 4>(g, a, s);
+      case 5: return launch_gemm_t<T, TA, 1, 5, 4>(g, a, s);
+      case 8: return launch_gemm_t<T, TA, 1, 8, 4>(g, a, s);
+      case 9: return launch_gemm_t<T, TA, 1, 9, 4>(g, a, s);
+      case 10: return launch_gemm_t<T, TA, 1, 10, 4>(g, a, s);
+      default: return launch_gemm_t<T, TA, 1, 16, 4>(g, a, s);
+    }
+  }
+  if (g.KSW == 4 && g.MT == 2) {
+    switch (g.NT) {
+      case 2: return launch_gemm_t<T, TA, 2, 2, 4>(g, a, s);
+      case 4: return launch_gemm_t<T, TA, 2, 4, 4>(g, a, s);
+      case 5: return launch_gemm_t<T, TA, 2, 5, 4>(g, a, s);
+      default: return launch_gemm_t<T, TA, 2, 8, 4>(g, a, s);
+    }
+  }
+  if (g.KSW == 4) {
+    return g.NT == 2 ? launch_gemm_t<T, TA, 4, 2, 4>(g, a, s) : launch_gemm_t<T, TA, 4, 4, 4>(g, a, s);
+  }
+  return launch_gemm_t<T, TA, 4, 4, 1>(g, a, s);
+}
+
+hipError_t launch_gemm(const GemmPlan& g, bool bf16, bool a_f32, const void* A, int lda, const void* Wp, float* part,
+                       int32_t* counters, const EpiArgs& e, hipStream_t s) {
+  (void)counters;
+  GemmArgs a{};
+  a.A = A;
+  a.lda = lda;
+  a.Wp = Wp;
+  a.kblocks = g.kblocks;
+  a.ntiles = g.ntiles;
+  a.Np = g.Np;
+  a.ksplit = g.ksplit;
+  a.kb_per_split = g.kb_per_split;
+  a.part = part;
+  a.e = e;
+  a.e.M = g.M;
+  a.e.N = g.N;
+  if (bf16) {
+    return a_f32 ? launch_gemm_sel<__bf16, float>(g, a, s) : launch_gemm_sel<__bf16, __bf16>(g, a, s);
+  }
+  return launch_gemm_sel<float, float>(g, a, s);
 }
 
 // --------------------------------------------------------------------------
@@ -257,14 +359,14 @@ __global__ __launch_bounds__(256) void pack_kernel(AbsorbArgs a, int mode, int K
   const size_t total = (size_t)Kp * Np;
   const size_t p = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (p >= total) return;
-  // invert packed_index: p = ((nt * KBLK + kb) * 64 + lane) * KPL + j
+  // invert packed_index: p = ((kb * NTT + nt) * 64 + lane) * KPL + j
   const int j = (int)(p % F::KPL);
   const size_t q = p / F::KPL;
   const int lane = (int)(q % 64);
   const size_t r = q / 64;
-  const int kblk = Kp / F::KB;
-  const int kb = (int)(r % kblk);
-  const int nt = (int)(r / kblk);
+  const int ntt = Np / 16;
+  const int nt = (int)(r % ntt);
+  const int kb = (int)(r / ntt);
   const int n = nt * 16 + (lane & 15);
   const int k = kb * F::KB + (lane >> 4) * F::KPL + j;
   const T* src = nullptr;
@@ -300,7 +402,7 @@ struct ProdArgs {
   const void* Ab; long a_hs, a_rs, a_ds;
   const void* Bb; long b_hs, b_ds, b_cs;
   int H, rows, cols, kd;
-  int k_hs, n_hs, Kp;
+  int k_hs, n_hs, Np;   // Np: padded column count of the packed output
   void* out;
 };
 
@@ -341,7 +443,7 @@ __global__ __launch_bounds__(256) void absorb_product_kernel(ProdArgs p) {
   for (int i = 0; i < 4; ++i) {
     const int rr = rt * 16 + 4 * (lane >> 4) + i;
     if (rr < p.rows)
-      out[packed_index(h * p.k_hs + rr, h * p.n_hs + cc, p.Kp, F::KB, F::KPL)] = from_f32<T>(acc[i]);
+      out[packed_index(h * p.k_hs + rr, h * p.n_hs + cc, p.Np, F::KB, F::KPL)] = from_f32<T>(acc[i]);
   }
 }
 
@@ -371,7 +473,7 @@ static hipError_t absorb_t(const AbsorbArgs& a, hipStream_t s) {
     p.Ab = a.W_UQ; p.a_hs = a.d_nope; p.a_rs = (long)a.H * a.d_nope; p.a_ds = 1;
     p.Bb = a.W_UK; p.b_hs = a.d_nope; p.b_ds = 1; p.b_cs = (long)a.H * a.d_nope;
     p.H = a.H; p.rows = a.d_q_latent; p.cols = a.d_latent; p.kd = a.d_nope;
-    p.k_hs = 0; p.n_hs = R; p.Kp = ceil_div(a.d_q_latent, F::KB) * F::KB; p.out = a.P_QC;
+    p.k_hs = 0; p.n_hs = R; p.Np = ceil_div(a.H * R, 16) * 16; p.out = a.P_QC;
     const long tiles = (long)a.H * ceil_div(p.rows, 16) * ceil_div(p.cols, 16);
     hipLaunchKernelGGL(absorb_product_kernel<T>, dim3((unsigned)((tiles + 3) / 4)), dim3(256), 0, s, p);
     hipError_t err = hipGetLastError();
@@ -383,7 +485,7 @@ static hipError_t absorb_t(const AbsorbArgs& a, hipStream_t s) {
     p.Ab = a.W_UV; p.a_hs = a.d_v; p.a_rs = (long)a.H * a.d_v; p.a_ds = 1;
     p.Bb = a.W_O; p.b_hs = (long)a.d_v * a.d_model; p.b_ds = a.d_model; p.b_cs = 1;
     p.H = a.H; p.rows = a.d_latent; p.cols = a.d_model; p.kd = a.d_v;
-    p.k_hs = a.d_latent; p.n_hs = 0; p.Kp = ceil_div(a.H * a.d_latent, F::KB) * F::KB; p.out = a.P_O;
+    p.k_hs = a.d_latent; p.n_hs = 0; p.Np = ceil_div(a.d_model, 16) * 16; p.out = a.P_O;
     const long tiles = (long)a.H * ceil_div(p.rows, 16) * ceil_div(p.cols, 16);
     hipLaunchKernelGGL(absorb_product_kernel<T>, dim3((unsigned)((tiles + 3) / 4)), dim3(256), 0, s, p);
     hipError_t err = hipGetLastError();

@@ -8,31 +8,20 @@
 namespace mla {
 
 // ---------------------------------------------------------------- GEMM ----
-// y[M][N] = A[M][K] * W[K][N] with W in the packed fragment layout.
-// Work split: n-groups of NT 16-column tiles, m-groups of MT 16-row tiles,
-// ksplit slices of the K range.  fp32 partial sums go to part[ks][M][Np].
-struct GemmPlan {
-  int M, K, N;       // logical sizes
-  int Kp, Np;        // padded sizes of the packed weight
-  int KB;            // k per MFMA (32 bf16, 4 fp32)
-  int kblocks, ntiles;
-  int NT, MT, ngroups, mgroups;
-  int ksplit, kb_per_split;
-  size_t part_bytes;
-};
-
-GemmPlan plan_gemm(int M, int K, int N, bool bf16, int n_cu);
-
-// A is T (a_f32 == false) or fp32 (a_f32 == true); Wp is T.
-hipError_t launch_gemm(const GemmPlan& g, bool bf16, bool a_f32, const void* A, int lda,
-                       const void* Wp, float* part, hipStream_t s);
-
+// y[M][N] = A[M][K] * W[K][N] with W in the packed fragment layout, followed
+// by an epilogue (store / RoPE / cache append).  One block computes a tile of
+// MT*16 rows x NGW*NT*16 columns over one K slice:
+//   KSW = 4 (decode, M <= 16): the block's 4 waves split the K slice and are
+//            summed through LDS;
+//   KSW = 1 (M > 16): the 4 waves take 4 neighbouring column groups.
+// With ksplit > 1 slices, each block leaves an fp32 partial tile in the
+// workspace and the last block to finish a tile (atomic counter, reset by
+// that block) sums the slices in order and applies the epilogue.
 enum EpiMode { EPI_F32 = 0, EPI_STORE_T = 1, EPI_Q = 2, EPI_APPEND = 3 };
 
 struct EpiArgs {
   int mode;
-  int M, N, Np, ksplit;
-  const float* part;
+  int M, N;
   void* out;            // EPI_F32: float[M][N]; EPI_STORE_T / EPI_Q: T[M][N]
   // RoPE (EPI_Q, EPI_APPEND)
   int d_latent, d_rope, row;   // row = d_latent + d_rope
@@ -47,7 +36,23 @@ struct EpiArgs {
   int32_t* err;
 };
 
-hipError_t launch_epilogue(const EpiArgs& e, bool bf16, hipStream_t s);
+struct GemmPlan {
+  int M, K, N;       // logical sizes
+  int Kp, Np;        // padded sizes of the packed weight
+  int KB;            // k per MFMA (32 bf16, 4 fp32)
+  int kblocks, ntiles;
+  int MT, NT, KSW;
+  int gx, gy;        // blocks over columns / rows
+  int ksplit, kb_per_split;
+  size_t part_bytes; // fp32 partial tiles (ksplit > 1)
+  int counters;      // tile counters (ksplit > 1)
+};
+
+GemmPlan plan_gemm(int M, int K, int N, bool bf16, int n_cu);
+
+// A is T (a_f32 == false) or fp32 (a_f32 == true); Wp is T.
+hipError_t launch_gemm(const GemmPlan& g, bool bf16, bool a_f32, const void* A, int lda, const void* Wp, float* part,
+                       int32_t* counters, const EpiArgs& e, hipStream_t s);
 
 // ------------------------------------------------------------- absorb ----
 struct AbsorbArgs {

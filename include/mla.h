@@ -128,10 +128,12 @@ const char *mla_version(void);
  *   [3] W_UVO  : K = H * d_L,  N = d_model    row h*d_L + c:
  *                (W_UV[h] W_O[h])[c, :]  (merged, output side)
  * Packed order of a logical K x N matrix W (y = x W): element (k, n) sits at
- *   ((n/16) * (Kp/KB) + k/KB) * 64*KPL + ((n%16) + 16*((k%KB)/KPL)) * KPL + k%KPL
- * with KB = 32, KPL = 8 for bf16 (KB = 4, KPL = 1 for fp32) and Kp = K
- * rounded up to KB; padding is zero.  Each 64*KPL block is exactly one MFMA
- * B-operand fragment. Offsets are 256-byte aligned. */
+ *   ((k/KB) * (Np/16) + n/16) * 64*KPL + ((n%16) + 16*((k%KB)/KPL)) * KPL + k%KPL
+ * with KB = 32, KPL = 8 for bf16 (KB = 4, KPL = 1 for fp32), Np = N rounded
+ * up to 16 and K rounded up to KB; padding is zero.  Each 64*KPL block is
+ * exactly one MFMA B-operand fragment (16 columns x KB rows), and the
+ * fragments of neighbouring column tiles at one k-block are adjacent.
+ * Offsets are 256-byte aligned. */
 mla_status mla_absorbed_layout(const mla_dims *dims, size_t offsets[4], size_t bytes[4], size_t *total);
 
 /* One-time weight absorption: fills `absorbed` (size from

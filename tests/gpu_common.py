@@ -106,6 +106,6 @@ def unpack(buf: np.ndarray, K: int, N: int, bf16: bool) -> np.ndarray:
     """Packed fragment order (see include/mla.h) -> row-major [K, N]."""
     KB, KPL = (32, 8) if bf16 else (4, 1)
     Kp, Np = -(-K // KB) * KB, -(-N // 16) * 16
-    a = buf.reshape(Np // 16, Kp // KB, KB // KPL, 16, KPL)      # [nt, kb, g, n16, j]
-    a = a.transpose(1, 2, 4, 0, 3).reshape(Kp, Np)                # [kb, g, j, nt, n16]
+    a = buf.reshape(Kp // KB, Np // 16, KB // KPL, 16, KPL)      # [kb, nt, g, n16, j]
+    a = a.transpose(0, 2, 4, 1, 3).reshape(Kp, Np)                # [kb, g, j, nt, n16]
     return a[:K, :N]
