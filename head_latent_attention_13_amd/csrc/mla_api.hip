@@ -122,7 +122,7 @@ WsLayout ws_layout(const mla_dims* d, int batch, int n_q) {
 
   const int HG = attn_head_group(bf);
   const size_t U = (size_t)M * ((H + HG - 1) / HG);
-  W.tile_off = o; o = align256(o + (U + 1) * 4);
+  W.tile_off = o; o = align256(o + attn_sched_ints((int)U, W.G) * 4);
   const size_t slots = (size_t)W.G + U;
   W.attn_o = o; o = align256(o + slots * HG * d->d_latent * 4);
   W.attn_lse = o; o = align256(o + slots * HG * 4);
@@ -200,7 +200,7 @@ mla_status attention_impl(const mla_dims* d, const WsLayout& W, const void* q, c
   a.n_q = n_q;
   a.H = d->n_heads;
   a.V = batch * n_q;
-  a.tile_off = reinterpret_cast<int32_t*>(ws + W.tile_off);
+  a.sched = reinterpret_cast<int32_t*>(ws + W.tile_off);  // plan storage, carved up by the launcher
   a.o_lat = o_lat;
   a.lse = lse;
   a.part_o = reinterpret_cast<float*>(ws + W.attn_o);

@@ -17,19 +17,23 @@
 // sequence cut by a work-group boundary leaves one (O, LSE) partial per
 // piece, combined afterwards with a log-sum-exp merge.
 //
-// Inside a work-group (8 waves for 128 heads):
+// Inside a work-group (4 waves, all 128 heads of the sequence):
 //   * 32-token tiles are DMA'd global -> LDS (global_load_lds, 16 B/lane)
-//     through a 3-stage ring, with a 16-byte-chunk XOR swizzle so MFMA
-//     operand reads are bank-conflict free.  Rows past the visible length
+//     through a 3-stage ring.  A tile is stored as 9 column blocks of 64
+//     latent/rope values (128 B per row) with a 16-byte-chunk XOR swizzle;
+//     wave w DMAs rows 8w..8w+7 of every block, so its per-lane source
+//     offset is one register plus immediates.  Rows past the visible length
 //     are DMA'd from a zero buffer, never from the cache.
-//   * S phase: wave w owns heads 16w..16w+15; S^T[32 tokens x 16 heads] =
-//     tile . q^T on MFMA (q held in registers for the whole segment);
-//     online-softmax statistics per head with cross-lane reductions; P is
-//     written to LDS in bf16.
-//   * PV phase: wave w owns latent columns [64w, 64w+64) for all 128 heads;
-//     O[128 x 64] += P[128 x 32] . tile[32 x 64-col slice] on MFMA.  Each
-//     tile column is read from LDS by exactly one wave.
+//   * Score phase: wave w owns heads 32w..32w+31; S^T[32 tokens x 32 heads]
+//     = tile . q^T on 32x32x16 bf16 MFMA, q held in registers for the whole
+//     segment; online-softmax statistics per head (lanes l and l^32 share a
+//     head); P goes to LDS in bf16.
+//   * PV phase: wave w owns latent columns [128w, 128w+128) for all 128
+//     heads: O[128 x 128] (AGPRs) += P[128 x 32] . tile[32 x 128-col slice];
+//     each tile column is read from LDS by exactly one wave.
 #include <math.h>
+
+#include <type_traits>
 
 #include "mla_common.h"
 #include "mla_internal.h"
@@ -40,135 +44,241 @@ static __device__ __attribute__((aligned(16))) unsigned char g_zero_rows[64 * 16
 
 #define MLA_CONST_PTR(p) ((const __attribute__((address_space(4))) int32_t*)(p))
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// 32x32 MFMA of the attention kernel.  Lane l holds A[l%32][(l/32)*KPL + j],
+// B[(l/32)*KPL + j][l%32] and D[8*(r/4) + 4*(l/32) + r%4][l%32], r < 16.
+//
+// bf16: the 128 x 128 fp32 O block of a wave fills all 256 AGPRs, so the
+// MFMAs are issued through inline asm with explicit register classes: the
+// score chain accumulates in VGPRs (its result feeds VALU code), the O
+// tiles in AGPRs.  The asm is volatile, so LDS loads stay where the source
+// puts them (the loops below prefetch operands a fixed distance ahead).
+// The compiler's hazard tracking does not see into asm, so each asm carries
+// the wait states its consumers need:
+//   * a VALU-written B operand needs 2 wait states before an MFMA reads it;
+//   * an MFMA result needs >= 18 wait states before VALU or copies read it
+//     (24 are issued: s_nop 15 + s_nop 7);
+//   * back-to-back MFMAs accumulating into the same registers need none.
+template <typename T>
+struct Mfma32;
+template <>
+struct Mfma32<__bf16> {
+  static constexpr int KB = 16, KPL = 8;
+  using frag = bf16x8;
+  // s = a.b (fresh accumulator in VGPRs)
+  __device__ static inline f32x16 first(frag a, frag b) {
+    f32x16 d;
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+    return d;
+  }
+  // s += a.b, VGPR accumulator
+  __device__ static inline void acc_v(f32x16& s, frag a, frag b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a), "v"(b));
+  }
+  // s += a.b, last of a chain: the result is readable by VALU afterwards
+  __device__ static inline void acc_v_last(f32x16& s, frag a, frag b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 15\n\ts_nop 7" : "+v"(s) : "v"(a), "v"(b));
+  }
+  // o += a.b, AGPR accumulator; b was just assembled by VALU code
+  __device__ static inline void acc_a_fresh_b(f32x16& o, frag a, frag b) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(a), "v"(b));
+  }
+  __device__ static inline void acc_a(f32x16& o, frag a, frag b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(a), "v"(b));
+  }
+  __device__ static inline frag zero() { return Mfma<__bf16>::zero(); }
+};
+template <>
+struct Mfma32<float> {
+  static constexpr int KB = 2, KPL = 1;
+  using frag = float;
+  __device__ static inline f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+  __device__ static inline f32x16 first(frag a, frag b) { return mma(a, b, f32x16{}); }
+  __device__ static inline void acc_v(f32x16& s, frag a, frag b) { s = mma(a, b, s); }
+  __device__ static inline void acc_v_last(f32x16& s, frag a, frag b) { s = mma(a, b, s); }
+  __device__ static inline void acc_a_fresh_b(f32x16& o, frag a, frag b) { o = mma(a, b, o); }
+  __device__ static inline void acc_a(f32x16& o, frag a, frag b) { o = mma(a, b, o); }
+  __device__ static inline frag zero() { return 0.0f; }
+};
+
+// o[r] *= al[r] for an AGPR-resident accumulator tile, one element at a
+// time through a scratch VGPR (keeps the tile in place).
+__device__ inline void o_scale_tile(f32x16& o, const float (&al)[16]) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float e = o[r], t;
+    asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                 : "+a"(e), "=&v"(t)
+                 : "v"(al[r]));
+    o[r] = e;
+  }
+}
+
+// Wait states between the last asm MFMA into the O block and any other
+// access to it (rescale, final read); a no-op for compiler-issued MFMAs.
+template <typename T, int NTH, int NCT>
+__device__ inline void o_settle(f32x16 (&O)[NTH][NCT]) {
+  if constexpr (sizeof(T) == 2 && NTH == 4 && NCT == 4) {
+    asm volatile("s_nop 15\n\ts_nop 7"
+                 : "+a"(O[0][0]), "+a"(O[0][1]), "+a"(O[0][2]), "+a"(O[0][3]), "+a"(O[1][0]), "+a"(O[1][1]),
+                   "+a"(O[1][2]), "+a"(O[1][3]), "+a"(O[2][0]), "+a"(O[2][1]), "+a"(O[2][2]), "+a"(O[2][3]),
+                   "+a"(O[3][0]), "+a"(O[3][1]), "+a"(O[3][2]), "+a"(O[3][3]));
+  }
+}
+
 template <typename T_, int HP_, int NW_, int DL_, int DR_, int NSTAGE_>
 struct AttnCfg {
   using T = T_;
-  using F = Mfma<T>;
-  // HP = heads handled by one work-group (one head group)
+  using F = Mfma32<T>;
   static constexpr int HP = HP_, NW = NW_, DL = DL_, DR = DR_, R = DL_ + DR_;
   static constexpr int ES = (int)sizeof(T);
   static constexpr int TILE = 32;
   static constexpr int NSTAGE = NSTAGE_;
   static constexpr int NTHR = NW * 64;
-  static constexpr int NHT = HP / 16;        // head tiles
-  static constexpr int HTW = NHT / NW;       // head tiles per wave in the score phase
+  static constexpr int NTH = HP / 32;        // 32-head tiles
   static constexpr int KB = F::KB, KPL = F::KPL;
-  static constexpr int RK = R / KB;          // MFMA k-steps over one row
-  static constexpr int CPW = DL / NW;        // latent columns per wave in the PV phase
-  static constexpr int NCT = CPW / 16;
+  static constexpr int RK = R / KB;          // score k-steps over one row
+  static constexpr int PV_KS = TILE / KB;    // PV k-steps over one tile
+  static constexpr int CPW = DL / NW;        // latent columns per wave (PV phase)
+  static constexpr int NCT = CPW / 32;       // 32-column tiles per wave
   static constexpr int ROW_BYTES = R * ES;
   static constexpr int ROW_CHUNKS = ROW_BYTES / 16;
-  static constexpr bool SWZ = (ROW_CHUNKS % 8) == 0;
-  // closed-form swizzled offsets (bf16 rows, 4 chunks per k-step, 64-column slices)
-  static constexpr bool FAST = SWZ && KPL == 8 && (CPW % 64) == 0;
+  // column-block layout with swizzle (bf16, 64-value blocks, 128-col slices)
+  static constexpr bool FAST = (ES == 2) && (ROW_CHUNKS % 8 == 0) && (CPW % 64 == 0) && (NW == 4);
+  static constexpr int BLOCK_BYTES = TILE * 128;
   static constexpr int TILE_BYTES = TILE * ROW_BYTES;
   static constexpr int NINST = TILE_BYTES / 1024;
   static constexpr int PSTR = TILE + 16 / ES;
-  static constexpr int PV_KS = TILE / KB;
-  static constexpr int OFF_P = NSTAGE * TILE_BYTES;
+  // FAST: the last QL 64-wide column blocks of q sit in LDS ([block][head]
+  // rows of 128 B, swizzled like the tiles); the rest stays in registers
+  static constexpr int QL = FAST ? 2 : 0;
+  static constexpr int RKQ = RK - QL * 4;  // q fragments held in registers
+  static constexpr int OFF_Q = NSTAGE * TILE_BYTES;
+  static constexpr int Q_BLOCK_BYTES = HP * 128;
+  static constexpr int OFF_P = OFF_Q + QL * Q_BLOCK_BYTES;
   static constexpr int OFF_ALPHA = OFF_P + HP * PSTR * ES;
   static constexpr int OFF_M = OFF_ALPHA + HP * 4;
   static constexpr int OFF_L = OFF_M + HP * 4;
   static constexpr int OFF_FLAG = OFF_L + HP * 4;
-  static constexpr int LDS_BYTES = OFF_FLAG + NHT * 4;
-  static_assert(R % KB == 0, "row width must be a multiple of the MFMA k");
-  static_assert(TILE_BYTES % 1024 == 0, "tile must be whole 1 KB DMA blocks");
-  static_assert(NINST % NW == 0, "DMA blocks must split evenly over waves");
-  static_assert(NHT % NW == 0, "head tiles must split evenly over waves");
-  static_assert(DL % (NW * 16) == 0, "latent columns must split evenly over waves");
-  static_assert(TILE % KB == 0, "tile must be whole MFMA k-steps");
+  static constexpr int LDS_BYTES = OFF_FLAG + NTH * 4;
+  static_assert(NTH == NW, "one 32-head tile per wave in the score phase");
+  static_assert(R % KB == 0 && TILE % KB == 0, "whole MFMA k-steps");
+  static_assert(TILE_BYTES % 1024 == 0 && NINST % NW == 0, "tile must be whole 1 KB DMA blocks per wave");
+  static_assert(DL % (NW * 32) == 0, "latent columns must split evenly over waves");
   static_assert(ROW_BYTES % 16 == 0, "rows must be whole 16 B chunks");
+  static_assert(!FAST || NINST == 4 * (ROW_CHUNKS / 8), "FAST: 4 DMA blocks per column block");
 };
 
-// One work-group = one head group of 64 heads: 4 waves x 16 heads in the
-// score phase, 4 waves x 128 latent columns in the PV phase (O: 64 x 512
-// fp32 = 128 accumulator registers per lane).  Both head groups of a tile
-// range run on the same XCD, so each tile is fetched from HBM once.
-using CfgBf16 = AttnCfg<__bf16, 64, 4, 512, 64, 3>;
-using CfgF32 = AttnCfg<float, 16, 1, 32, 8, 3>;
+// 128 heads per work-group: 4 waves x 32 heads (score phase), 4 waves x 128
+// latent columns (PV phase); the fp32 O accumulators (128 x 512) fill the
+// AGPRs of the four waves.
+using CfgBf16 = AttnCfg<__bf16, 128, 4, 512, 64, 3>;
+using CfgF32 = AttnCfg<float, 32, 1, 32, 8, 3>;
 
 // Softmax statistics are only rebased when a head's running max grows by
 // more than this (log2 units); P stays <= 2^8, exact in bf16 and fp32.
 constexpr float kRescaleSlack = 8.0f;
 
-// 16-byte-chunk swizzle of a tile row: logical chunk c of row r sits at
-// chunk c ^ swz(r).  Rows 8g+j of the four lane groups of a transposed PV
-// read, and the 8 rows of one ds_read_b128 pass of the score phase, land in
-// distinct banks.
-__device__ inline int swz(int r) { return (r ^ ((r >> 3) << 1)) & 7; }
+// 16-byte-chunk swizzle inside a 128-byte block row: logical chunk c of
+// tile row r sits at chunk c ^ swz(r).  Rows 128 B apart alternate between
+// the two halves of the 64 banks.  swz permutes the 8 same-parity rows of a
+// 16-row group onto 8 distinct chunks (a 16-lane ds_read_b128 pass of the
+// score phase is conflict-free), and rows r, r+2 (r = 0 mod 4) differ in
+// bit 2, so the 4-row x 32-byte footprint of a transposing PV read never
+// puts two rows on the same banks.
+__device__ inline int swz(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
 
+// Byte offset of element e of tile row r in an LDS stage.
 template <class C>
 __device__ inline int lds_off(int r, int e) {
   const int byte = e * C::ES;
-  int chunk = byte >> 4;
-  if constexpr (C::SWZ) chunk ^= swz(r);
-  return r * C::ROW_BYTES + (chunk << 4) + (byte & 15);
+  if constexpr (C::FAST) {
+    const int c = byte >> 4;
+    return (c >> 3) * C::BLOCK_BYTES + r * 128 + (((c & 7) ^ swz(r)) << 4) + (byte & 15);
+  } else {
+    return r * C::ROW_BYTES + byte;
+  }
 }
 
-// max / sum with the lanes 16 and 32 apart (gfx950 permlane swaps, no LDS)
-__device__ inline float max_xor16_32(float x) {
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+__device__ inline float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ inline float sum_xor16_32(float x) {
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+__device__ inline float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__device__ inline void vm_wait_rt(int n) {
-  switch (n) {
-    case 0: vm_wait<0>(); break;
-    case 1: vm_wait<1>(); break;
-    case 2: vm_wait<2>(); break;
-    case 3: vm_wait<3>(); break;
-    case 4: vm_wait<4>(); break;
-    case 5: vm_wait<5>(); break;
-    case 6: vm_wait<6>(); break;
-    case 7: vm_wait<7>(); break;
-    case 8: vm_wait<8>(); break;
-    case 9: vm_wait<9>(); break;
-    case 10: vm_wait<10>(); break;
-    case 11: vm_wait<11>(); break;
-    case 12: vm_wait<12>(); break;
-    case 16: vm_wait<16>(); break;
-    case 18: vm_wait<18>(); break;
-    default: vm_wait<0>(); break;
+// Raw buffer resource over [base, base + bytes): loads past the end return
+// zeros.  Word 3 selects 32-bit data format (raw untyped access).
+// The arguments must be wave-uniform; they are pinned to scalar registers.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p), hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  void* b = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(b, (short)0, __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+// DMA one 32-row tile into an LDS stage with buffer loads whose record
+// count is the tile's visible bytes: rows at or past `vis`, a page id
+// outside the pool, and a tile past the end of the segment (`live` false)
+// all read as zeros.  Every call issues the same NINST / NW loads per wave,
+// so the pipeline can wait on a constant count.
+template <class C>
+__device__ inline void issue_tile(const AttnArgs& a, unsigned char* stage, int b, int k, int vis, int wave,
+                                  int lane, int dma_off, bool live) {
+  const int t0 = k * C::TILE;
+  const unsigned char* gbase = reinterpret_cast<const unsigned char*>(a.pool);
+  bool ok = live;
+  if (live) {
+    if (a.paged) {
+      const int pg = MLA_CONST_PTR(a.page_table)[(size_t)b * a.max_pages + t0 / a.page_size];
+      ok = (pg >= 0) && (pg < a.n_pages);
+      gbase += ((size_t)(ok ? pg : 0) * a.page_size + (t0 % a.page_size)) * (size_t)C::ROW_BYTES;
+    } else {
+      gbase += ((size_t)b * a.s_max + t0) * (size_t)C::ROW_BYTES;
+    }
+  }
+  const int nbytes = ok ? min(max(vis - t0, 0), C::TILE) * C::ROW_BYTES : 0;
+  const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(gbase, nbytes);
+  if constexpr (C::FAST) {
+    // wave w fills rows 8w + lane/8 of every column block; dma_off holds the
+    // lane's row and swizzled chunk, block k adds 128 B in global memory
+#pragma unroll
+    for (int kk = 0; kk < C::NINST / C::NW; ++kk)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, MLA_LDS_PTR(stage + (wave + 4 * kk) * 1024), 16,
+                                               dma_off + kk * 128, 0, 0, 0);
+  } else {
+    // row-major rows; 16-byte chunk p of the tile goes to LDS byte 16 p
+#pragma unroll
+    for (int kk = 0; kk < C::NINST / C::NW; ++kk) {
+      const int in = wave + kk * C::NW;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, MLA_LDS_PTR(stage + in * 1024), 16, (in * 64 + lane) * 16, 0, 0,
+                                               0);
+    }
   }
 }
 
-// DMA one 32-row tile into an LDS stage.  Every wave issues the same number
-// of load instructions on every call, so the per-wave vmcnt bookkeeping of
-// the pipeline is exact.  Rows at or past `vis` (and rows of a page id
-// outside the pool) are DMA'd from a zero buffer instead of the cache.
+// DMA the trailing QL column blocks of q for this wave's 32 heads into LDS
+// (swizzled 128-byte rows, one per head); heads past H read as zeros.
 template <class C>
-__device__ inline void issue_tile(const AttnArgs& a, unsigned char* stage, int b, int k, int vis, int wave,
-                                  int lane) {
-  const int t0 = k * C::TILE;
-  const unsigned char* gbase;
-  bool ok = true;
-  if (a.paged) {
-    const int pg = MLA_CONST_PTR(a.page_table)[(size_t)b * a.max_pages + t0 / a.page_size];
-    ok = (pg >= 0) && (pg < a.n_pages);
-    gbase = reinterpret_cast<const unsigned char*>(a.pool) +
-            ((size_t)(ok ? pg : 0) * a.page_size + (t0 % a.page_size)) * (size_t)C::ROW_BYTES;
-  } else {
-    gbase = reinterpret_cast<const unsigned char*>(a.pool) + ((size_t)b * a.s_max + t0) * (size_t)C::ROW_BYTES;
-  }
+__device__ inline void issue_q_tail(const AttnArgs& a, unsigned char* smem, int v, int h_base, int wave, int lane) {
+  using T = typename C::T;
+  const int h0 = h_base + wave * 32;
+  const __amdgpu_buffer_rsrc_t qr = make_rsrc(
+      reinterpret_cast<const T*>(a.q) + ((size_t)v * a.H + min(h0, a.H)) * C::R, max(min(a.H - h0, 32), 0) * C::ROW_BYTES);
 #pragma unroll
-  for (int inst = 0; inst < C::NINST / C::NW; ++inst) {
-    const int in = wave + inst * C::NW;
-    const int p = in * 64 + lane;
-    const int r = p / C::ROW_CHUNKS, s = p % C::ROW_CHUNKS;
-    const int c = C::SWZ ? (s ^ swz(r)) : s;
-    const bool valid = ok && (t0 + r < vis);
-    const void* src =
-        valid ? (const void*)(gbase + r * C::ROW_BYTES + c * 16) : (const void*)(g_zero_rows + lane * 16);
-    __builtin_amdgcn_global_load_lds(src, MLA_LDS_PTR(stage + in * 1024), 16, 0, 0);
-  }
+  for (int qb = 0; qb < C::QL; ++qb)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int r = 8 * i4 + (lane >> 3);  // head row within the wave
+      const int c = (lane & 7) ^ swz(r);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, MLA_LDS_PTR(smem + C::OFF_Q + qb * C::Q_BLOCK_BYTES + wave * 4096 + i4 * 1024),
+                                               16, r * C::ROW_BYTES + ((C::RKQ / 4 + qb) * 64 + c * 8) * C::ES, 0, 0, 0);
+    }
 }
 
 // One 32-token tile of a segment: issue the DMA of a later tile into
@@ -180,132 +290,198 @@ __device__ inline void issue_tile(const AttnArgs& a, unsigned char* stage, int b
 template <class C>
 __device__ __forceinline__ void tile_step(const AttnArgs& a, unsigned char* __restrict__ dma_stage,
                                           const unsigned char* __restrict__ tb, typename C::T* __restrict__ p_s,
-                                          float* __restrict__ alpha_s, int* __restrict__ flag_s, bool issue,
+                                          const unsigned char* __restrict__ q_s, float* __restrict__ alpha_s,
+                                          int* __restrict__ flag_s, bool issue,
                                           int b, int k_issue, int tok0, int vis, int i, int wave, int lane,
-                                          const int (&s_base)[2][2], const int (&v_base)[4][2],
-                                          const typename C::F::frag (&qf)[C::HTW][C::RK], float (&m_run)[C::HTW],
-                                          float (&l_run)[C::HTW], f32x4 (&O)[C::NHT][C::NCT]) {
+                                          int dma_off, const int (&s_base)[4], const int (&tr_base)[2][2],
+                                          const typename C::F::frag (&qf)[C::RKQ], float& m_run, float& l_run,
+                                          f32x16 (&O)[C::NTH][C::NCT]) {
   using T = typename C::T;
   using F = typename C::F;
   using frag = typename F::frag;
-  const int g = lane >> 4, l16 = lane & 15;
-  if (issue) issue_tile<C>(a, dma_stage, b, k_issue, vis, wave, lane);
+  const int hi = lane >> 5, l32 = lane & 31;
+  issue_tile<C>(a, dma_stage, b, k_issue, vis, wave, lane, dma_off, issue);
 
-  // ---- S^T[32 tokens x 16 heads] = tile . q^T, per head tile ----------
-  // two accumulators per sub-tile (even / odd k-steps): four independent
-  // MFMA chains in flight
-  f32x4 sacc[C::HTW][2][2];
+  // ---- S^T[32 tokens x 32 heads] = tile . q^T (one MFMA chain) --------
+  auto a_frag = [&](int kb) -> frag {
+    if constexpr (C::FAST) {
+      return *reinterpret_cast<const frag*>(tb + s_base[kb & 3] + (kb >> 2) * C::BLOCK_BYTES);
+    } else {
+      return *reinterpret_cast<const frag*>(tb + lds_off<C>(l32, kb * C::KB + hi * C::KPL));
+    }
+  };
+  // q^T fragment kb: registers, or the LDS copy of the trailing blocks
+  auto b_frag = [&](int kb) -> frag {
+    if constexpr (C::QL > 0) {
+      if (kb >= C::RKQ) return *reinterpret_cast<const frag*>(q_s + (kb / 4 - C::RKQ / 4) * C::Q_BLOCK_BYTES + s_base[kb & 3]);
+    }
+    return qf[kb < C::RKQ ? kb : 0];
+  };
+  // operands are fetched SD k-steps ahead of their MFMA
+  constexpr int SD = 4;
+  frag ring_a[SD], ring_b[SD];
 #pragma unroll
-  for (int ht = 0; ht < C::HTW; ++ht)
-#pragma unroll
-    for (int u = 0; u < 2; ++u) sacc[ht][u][0] = sacc[ht][u][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int kb = 0; kb < SD; ++kb) {
+    ring_a[kb] = a_frag(kb);
+    if (kb >= C::RKQ) ring_b[kb] = b_frag(kb);
+  }
+  f32x16 s0;
 #pragma unroll
   for (int kb = 0; kb < C::RK; ++kb) {
-    frag a0, a1;
-    if constexpr (C::FAST) {
-      a0 = *reinterpret_cast<const frag*>(tb + s_base[0][kb & 1] + 128 * (kb >> 1));
-      a1 = *reinterpret_cast<const frag*>(tb + s_base[1][kb & 1] + 128 * (kb >> 1));
-    } else {
-      const int e = kb * C::KB + g * C::KPL;
-      a0 = *reinterpret_cast<const frag*>(tb + lds_off<C>(l16, e));
-      a1 = *reinterpret_cast<const frag*>(tb + lds_off<C>(16 + l16, e));
+    const frag av = ring_a[kb % SD];
+    const frag bv = kb >= C::RKQ ? ring_b[kb % SD] : qf[kb < C::RKQ ? kb : 0];
+    if (kb + SD < C::RK) {
+      ring_a[kb % SD] = a_frag(kb + SD);
+      if (kb + SD >= C::RKQ) ring_b[kb % SD] = b_frag(kb + SD);
     }
-#pragma unroll
-    for (int ht = 0; ht < C::HTW; ++ht) {
-      sacc[ht][0][kb & 1] = F::mma(a0, qf[ht][kb], sacc[ht][0][kb & 1]);
-      sacc[ht][1][kb & 1] = F::mma(a1, qf[ht][kb], sacc[ht][1][kb & 1]);
-    }
+    if (kb == 0)
+      s0 = F::first(av, bv);
+    else if (kb + 1 < C::RK)
+      F::acc_v(s0, av, bv);
+    else
+      F::acc_v_last(s0, av, bv);
   }
 
-  // ---- online softmax over this tile's 32 tokens, per head ------------
-  const bool tail = tok0 + C::TILE > vis;  // uniform: only the last tile is ragged
+  // ---- online softmax for head (wave*32 + l32) over the 32 tokens -------
+  // register r of this lane holds token 8*(r/4) + 4*hi + r%4
+  const int hl = wave * 32 + l32;
+  float x[16];
 #pragma unroll
-  for (int ht = 0; ht < C::HTW; ++ht) {
-    const int hl = (wave * C::HTW + ht) * 16 + l16;  // head within the group
-    float x[8];
+  for (int r = 0; r < 16; ++r) x[r] = s0[r] * a.scale_log2;
+  if (tok0 + C::TILE > vis) {  // uniform: only the last tile of a sequence is ragged
+    const int lim = vis - tok0 - 4 * hi;
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      x[ii] = (sacc[ht][0][0][ii] + sacc[ht][0][1][ii]) * a.scale_log2;
-      x[4 + ii] = (sacc[ht][1][0][ii] + sacc[ht][1][1][ii]) * a.scale_log2;
-    }
-    if (tail) {
-      const int lim = vis - tok0 - 4 * g;
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        if (ii >= lim) x[ii] = -INFINITY;
-        if (16 + ii >= lim) x[4 + ii] = -INFINITY;
-      }
-    }
-    float mloc = x[0];
-#pragma unroll
-    for (int ii = 1; ii < 8; ++ii) mloc = fmaxf(mloc, x[ii]);
-    mloc = max_xor16_32(mloc);
-    const bool rebase = mloc > m_run[ht] + kRescaleSlack;
-    float alpha = 1.f;
-    if (rebase) {
-      alpha = __builtin_amdgcn_exp2f(m_run[ht] - mloc);
-      m_run[ht] = mloc;
-    }
-    float psum = 0.f, pv[8];
-#pragma unroll
-    for (int ii = 0; ii < 8; ++ii) {
-      pv[ii] = __builtin_amdgcn_exp2f(x[ii] - m_run[ht]);
-      psum += pv[ii];
-    }
-    psum = sum_xor16_32(psum);
-    l_run[ht] = l_run[ht] * alpha + psum;
-    T* prow = p_s + (size_t)hl * C::PSTR;
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      prow[4 * g + ii] = from_f32<T>(pv[ii]);
-      prow[16 + 4 * g + ii] = from_f32<T>(pv[4 + ii]);
-    }
-    if (g == 0) alpha_s[hl] = alpha;
-    const bool any = __any(rebase);
-    if (lane == 0) flag_s[wave * C::HTW + ht] = any ? 1 : 0;
+    for (int r = 0; r < 16; ++r)
+      if (8 * (r >> 2) + (r & 3) >= lim) x[r] = -INFINITY;
   }
-  lds_barrier();
-
-  // ---- PV: O[group heads][this wave's columns] += P . tile ------------
-  if (i > 0) {
+  float mloc = x[0];
 #pragma unroll
-    for (int ht = 0; ht < C::NHT; ++ht) {
-      if (__builtin_amdgcn_readfirstlane(flag_s[ht])) {
-        const float4 a4 = *reinterpret_cast<const float4*>(alpha_s + ht * 16 + 4 * g);
-#pragma unroll
-        for (int ct = 0; ct < C::NCT; ++ct) {
-          O[ht][ct][0] *= a4.x;
-          O[ht][ct][1] *= a4.y;
-          O[ht][ct][2] *= a4.z;
-          O[ht][ct][3] *= a4.w;
-        }
-      }
-    }
+  for (int r = 1; r < 16; ++r) mloc = fmaxf(mloc, x[r]);
+  mloc = max_xor32(mloc);
+  const bool rebase = mloc > m_run + kRescaleSlack;
+  float alpha = 1.f;
+  if (rebase) {
+    alpha = __builtin_amdgcn_exp2f(m_run - mloc);
+    m_run = mloc;
   }
+  float psum = 0.f;
 #pragma unroll
-  for (int ks = 0; ks < C::PV_KS; ++ks) {
-    frag pa[C::NHT];
+  for (int r = 0; r < 16; ++r) {
+    x[r] = __builtin_amdgcn_exp2f(x[r] - m_run);
+    psum += x[r];
+  }
+  psum = sum_xor32(psum);
+  l_run = l_run * alpha + psum;
+  {
+    // P[head][token]: this lane's tokens 8*q4 + 4*hi + (0..3) are contiguous
+    T* prow = p_s + (size_t)hl * C::PSTR + 4 * hi;
 #pragma unroll
-    for (int ht = 0; ht < C::NHT; ++ht)
-      pa[ht] = *reinterpret_cast<const frag*>(p_s + (size_t)(ht * 16 + l16) * C::PSTR + ks * C::KB + g * C::KPL);
+    for (int q4 = 0; q4 < 4; ++q4) {
+      if constexpr (C::ES == 2) {
+        T v4[4];
 #pragma unroll
-    for (int ct = 0; ct < C::NCT; ++ct) {
-      frag bfr;
-      if constexpr (C::FAST) {
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj)
-          bfr[jj] = *reinterpret_cast<const T*>(tb + v_base[(ct & 3) ^ (jj >> 1)][jj & 1] + jj * C::ROW_BYTES +
-                                                128 * (ct >> 2));
-      } else if constexpr (C::KPL == 1) {
-        bfr = *reinterpret_cast<const T*>(tb + lds_off<C>(ks * C::KB + g, wave * C::CPW + ct * 16 + l16));
+        for (int u = 0; u < 4; ++u) v4[u] = from_f32<T>(x[4 * q4 + u]);
+        *reinterpret_cast<uint2*>(prow + 8 * q4) = *reinterpret_cast<const uint2*>(v4);
       } else {
 #pragma unroll
-        for (int jj = 0; jj < C::KPL; ++jj)
-          bfr[jj] = *reinterpret_cast<const T*>(
-              tb + lds_off<C>(ks * C::KB + g * C::KPL + jj, wave * C::CPW + ct * 16 + l16));
+        for (int u = 0; u < 4; ++u) prow[8 * q4 + u] = from_f32<T>(x[4 * q4 + u]);
       }
+    }
+  }
+  if (hi == 0) alpha_s[hl] = alpha;
+  const bool any = __any(rebase);
+  if (lane == 0) flag_s[wave] = any ? 1 : 0;
+  lds_barrier();
+
+  // ---- PV: O[all heads][this wave's columns] += P . tile ----------------
+  if (i > 0) {
+    int anyf = 0;
 #pragma unroll
-      for (int ht = 0; ht < C::NHT; ++ht) O[ht][ct] = F::mma(pa[ht], bfr, O[ht][ct]);
+    for (int ht = 0; ht < C::NTH; ++ht) anyf |= flag_s[ht];
+    if (__builtin_amdgcn_readfirstlane(anyf)) {
+      o_settle<T>(O);
+#pragma unroll
+      for (int ht = 0; ht < C::NTH; ++ht) {
+        // O row of register r: head ht*32 + 8*(r/4) + 4*hi + r%4
+        float al[16];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 a4 = *reinterpret_cast<const float4*>(alpha_s + ht * 32 + 8 * q4 + 4 * hi);
+          al[4 * q4 + 0] = a4.x;
+          al[4 * q4 + 1] = a4.y;
+          al[4 * q4 + 2] = a4.z;
+          al[4 * q4 + 3] = a4.w;
+        }
+#pragma unroll
+        for (int ct = 0; ct < C::NCT; ++ct) {
+          if constexpr (C::ES == 2) {
+            o_scale_tile(O[ht][ct], al);
+          } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) O[ht][ct][r] *= al[r];
+          }
+        }
+      }
+      o_settle<T>(O);
+    }
+  }
+  if constexpr (C::FAST) {
+    // B operand of (ks, ct): 8 rows x 1 column per lane, read with two
+    // transposing LDS loads (ds_read_b64_tr_b16).  In each 16-lane group the
+    // instruction hands lane i element i%4 of the 8-byte rows addressed by
+    // lanes i/4 + 4j (j = 0..3); lane s of the group therefore addresses row
+    // kbase + s/4, columns nbase + 4(s%4) .. +3, and lane i receives rows
+    // kbase..kbase+3 of column nbase + i.  tr_base holds those addresses.
+    // The loads of the next column tile are issued before the MFMAs of the
+    // current one.
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    auto b_load = [&](int ks, int ct, v4s (&bb)[2]) {
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+        bb[h2] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<__attribute__((address_space(3))) v4s*>(
+            MLA_LDS_PTR(tb + tr_base[ct & 1][h2] + (ct >> 1) * C::BLOCK_BYTES + ks * 16 * 128)));
+    };
+    v4s bb[2];
+    b_load(0, 0, bb);
+#pragma unroll
+    for (int ks = 0; ks < C::PV_KS; ++ks) {
+      frag pa[C::NTH];
+#pragma unroll
+      for (int ht = 0; ht < C::NTH; ++ht)
+        pa[ht] = *reinterpret_cast<const frag*>(p_s + (size_t)(ht * 32 + l32) * C::PSTR + ks * C::KB + hi * C::KPL);
+#pragma unroll
+      for (int ct = 0; ct < C::NCT; ++ct) {
+        const frag bfr = __builtin_bit_cast(frag, bb);
+        if (ct + 1 < C::NCT)
+          b_load(ks, ct + 1, bb);
+        else if (ks + 1 < C::PV_KS)
+          b_load(ks + 1, 0, bb);
+#pragma unroll
+        for (int ht = 0; ht < C::NTH; ++ht) F::acc_a(O[ht][ct], pa[ht], bfr);
+      }
+    }
+  } else {
+    // generic layout: one element per lane and k (KPL == 1 for fp32)
+#pragma unroll
+    for (int ks = 0; ks < C::PV_KS; ++ks) {
+      frag pa[C::NTH];
+#pragma unroll
+      for (int ht = 0; ht < C::NTH; ++ht)
+        pa[ht] = *reinterpret_cast<const frag*>(p_s + (size_t)(ht * 32 + l32) * C::PSTR + ks * C::KB + hi * C::KPL);
+#pragma unroll
+      for (int ct = 0; ct < C::NCT; ++ct) {
+        frag bfr;
+        if constexpr (C::KPL == 1) {
+          bfr = *reinterpret_cast<const T*>(tb + lds_off<C>(ks * C::KB + hi, wave * C::CPW + ct * 32 + l32));
+        } else {
+#pragma unroll
+          for (int j = 0; j < C::KPL; ++j)
+            bfr[j] = *reinterpret_cast<const T*>(tb + lds_off<C>(ks * C::KB + hi * C::KPL + j, wave * C::CPW + ct * 32 + l32));
+        }
+        F::acc_a_fresh_b(O[0][ct], pa[0], bfr);
+#pragma unroll
+        for (int ht = 1; ht < C::NTH; ++ht) F::acc_a(O[ht][ct], pa[ht], bfr);
+      }
     }
   }
 }
@@ -316,18 +492,18 @@ __global__ __launch_bounds__(C::NTHR, 1) void attn_split_kernel(AttnArgs a) {
   using F = typename C::F;
   using frag = typename F::frag;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int g = lane >> 4, l16 = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hi = lane >> 5, l32 = lane & 31;
   const int G = gridDim.x;
   // XCD-aware order: the hardware deals blocks round-robin over 8 XCDs, so
   // logical ranges are assigned such that neighbours share an XCD's L2.
   const int w = ((G & 7) == 0) ? ((int)(blockIdx.x & 7) * (G >> 3) + (int)(blockIdx.x >> 3)) : (int)blockIdx.x;
-  const int U = a.U;  // streams = (virtual sequence, head group) pairs
-  const int Ttot = MLA_CONST_PTR(a.tile_off)[U];
-  const int per = (Ttot + G - 1) / G;
-  const int g0 = w * per;
-  const int g1 = min(g0 + per, Ttot);
+  // work-group record: tile range and the first stream it touches
+  const auto wr = MLA_CONST_PTR(a.wrec) + 8 * w;
+  const int g0 = wr[0], g1 = wr[1];
   if (g0 >= g1) return;
+  int u = wr[2], tb0 = wr[3], tb1 = wr[4], vis = wr[5];
 
   float* alpha_s = reinterpret_cast<float*>(smem + C::OFF_ALPHA);
   float* m_s = reinterpret_cast<float*>(smem + C::OFF_M);
@@ -335,115 +511,122 @@ __global__ __launch_bounds__(C::NTHR, 1) void attn_split_kernel(AttnArgs a) {
   int* flag_s = reinterpret_cast<int*>(smem + C::OFF_FLAG);
   T* p_s = reinterpret_cast<T*>(smem + C::OFF_P);
 
-  // lane-constant LDS offsets (see the swizzle in issue_tile)
-  // s_base[sub-tile][k-step parity]: row l16 (+16) reads logical chunk
-  // 4*kb + g; v_base[t][p]: rows 8g+j of the transposed PV read, with
-  // t = (ct & 3) ^ (j >> 1) and p = j & 1 (closed forms of lds_off)
-  int s_base[2][2] = {{0, 0}, {0, 0}}, v_base[4][2] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};
+  // Lane-constant offsets (closed forms of lds_off, FAST layout):
+  //   dma_off      : global offset of this lane's 16 B in its wave's DMA rows
+  //   s_base[u]    : score-phase A fragment, k-step kb with kb%4 == u
+  //   tr_base[t][h]: transposing PV read of column tile ct (t = ct&1), rows
+  //                  16ks + 8(g>>1) + 4h + s/4 (g = lane/16, s = lane%16)
+  int dma_off = 0, s_base[4] = {0, 0, 0, 0}, tr_base[2][2] = {{0, 0}, {0, 0}};
   if constexpr (C::FAST) {
-    const int hb = l16 >> 3;
+    const int r = 8 * wave + (lane >> 3);
+    dma_off = r * C::ROW_BYTES + 16 * ((lane & 7) ^ swz(r));
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int r = l16 + 16 * sub;
+    for (int u = 0; u < 4; ++u) s_base[u] = l32 * 128 + 16 * ((2 * u + hi) ^ swz(l32));
+    const int g = lane >> 4, sl = lane & 15;
+    const int c_low = 2 * (g & 1) + ((sl & 3) >> 1);
 #pragma unroll
-      for (int par = 0; par < 2; ++par) s_base[sub][par] = r * C::ROW_BYTES + 16 * ((par * 4 + g) ^ swz(r));
-    }
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int par = 0; par < 2; ++par)
-        v_base[t][par] = g * 8 * C::ROW_BYTES + 16 * wave * (C::CPW / 8) + 16 * ((2 * (t ^ g) + (hb ^ par)) & 7) +
-                         2 * (l16 & 7);
+      for (int h2 = 0; h2 < 2; ++h2)
+        tr_base[t][h2] = 2 * wave * C::BLOCK_BYTES + (8 * (g >> 1) + 4 * h2 + (sl >> 2)) * 128 +
+                         64 * (t ^ ((sl >> 3) & 1)) + 16 * (c_low ^ (2 * (g >> 1) + h2)) + 8 * (sl & 1);
   }
 
-  // first stream holding tile g0
-  int lo = 0, hi = U;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (MLA_CONST_PTR(a.tile_off)[mid] <= g0) lo = mid; else hi = mid;
-  }
   constexpr int n_loads = C::NINST / C::NW;  // DMA instructions per tile and wave
 
-  int u = lo, gcur = g0;
+  int gcur = g0;
   while (gcur < g1) {
-    const int tb0 = MLA_CONST_PTR(a.tile_off)[u], tb1 = MLA_CONST_PTR(a.tile_off)[u + 1];
-    if (tb1 <= gcur) { ++u; continue; }
+    if (tb1 <= gcur) {  // next stream (an empty one has tb0 == tb1)
+      ++u;
+      const auto sr = MLA_CONST_PTR(a.srec) + 4 * u;
+      tb0 = sr[0];
+      tb1 = sr[1];
+      vis = sr[2];
+      continue;
+    }
     const int k0 = gcur - tb0, k1 = min(g1, tb1) - tb0;
     const bool whole = (k0 == 0) && (k1 == tb1 - tb0);
     const int cnt = k1 - k0;
     const int v = u / a.n_hg, hgrp = u - v * a.n_hg;
     const int h_base = hgrp * C::HP;
-    const int b = v / a.n_q, jq = v - b * a.n_q;
-    const int vis = MLA_CONST_PTR(a.kv_len)[b] - a.n_q + jq + 1;
+    const int b = v / a.n_q;
 
-    vm_wait<0>();
-    // q^T fragments of this wave's head tiles, kept in registers
-    frag qf[C::HTW][C::RK];
+    // tile 0 first, then q, then the other prologue tiles: the wait before
+    // tile 0 then also covers q, and later tiles stay in flight
+    issue_tile<C>(a, smem, b, k0, vis, wave, lane, dma_off, true);
+    asm volatile("" ::: "memory");  // keep the issue order: tile 0, q, tile 1
+    // q^T fragments of this wave's 32 heads: the first RKQ k-steps in
+    // registers, the trailing QL column blocks DMA'd into LDS (same
+    // swizzled 128-byte row layout as the tiles, one row per head).  Heads
+    // past H read the zero buffer.
+    frag qf[C::RKQ];
+    {
+      const int h = h_base + wave * 32 + l32;
+      const T* qp = (h < a.H) ? reinterpret_cast<const T*>(a.q) + ((size_t)v * a.H + h) * C::R + hi * C::KPL
+                              : reinterpret_cast<const T*>(g_zero_rows) + hi * C::KPL;
 #pragma unroll
-    for (int ht = 0; ht < C::HTW; ++ht) {
-      const int h = h_base + (wave * C::HTW + ht) * 16 + l16;
-      const T* qp = reinterpret_cast<const T*>(a.q) + ((size_t)v * a.H + min(h, a.H - 1)) * C::R + g * C::KPL;
-#pragma unroll
-      for (int kb = 0; kb < C::RK; ++kb) {
-        qf[ht][kb] = load_frag<T>(qp + kb * C::KB);
-        if (h >= a.H) qf[ht][kb] = F::zero();
-      }
+      for (int kb = 0; kb < C::RKQ; ++kb) qf[kb] = load_frag<T>(qp + kb * C::KB);
+      if constexpr (C::QL > 0) issue_q_tail<C>(a, smem, v, h_base, wave, lane);
     }
-    for (int s = 0; s < C::NSTAGE - 1 && s < cnt; ++s)
-      issue_tile<C>(a, smem + s * C::TILE_BYTES, b, k0 + s, vis, wave, lane);
+    asm volatile("" ::: "memory");
+    for (int s = 1; s < C::NSTAGE - 1; ++s)
+      issue_tile<C>(a, smem + s * C::TILE_BYTES, b, k0 + s, vis, wave, lane, dma_off, s < cnt);
 
-    float m_run[C::HTW], l_run[C::HTW];
+    float m_run = -1e30f, l_run = 0.f;
+    f32x16 O[C::NTH][C::NCT];
 #pragma unroll
-    for (int ht = 0; ht < C::HTW; ++ht) {
-      m_run[ht] = -1e30f;
-      l_run[ht] = 0.f;
-    }
-    f32x4 O[C::NHT][C::NCT];
+    for (int ht = 0; ht < C::NTH; ++ht)
 #pragma unroll
-    for (int ht = 0; ht < C::NHT; ++ht)
-#pragma unroll
-      for (int ct = 0; ct < C::NCT; ++ct) O[ht][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int ct = 0; ct < C::NCT; ++ct) O[ht][ct] = f32x16{};
 
-    for (int i = 0; i < cnt; ++i) {
-      const int st = i % C::NSTAGE;
-      vm_wait_rt(min(C::NSTAGE - 2, cnt - 1 - i) * n_loads);
+    auto step = [&](int i) {
+      // tiles i+1 .. i+NSTAGE-2 may stay in flight (zero-filled past the end)
+      vm_wait<(C::NSTAGE - 2) * n_loads>();
       lds_barrier();
-      const bool issue = i + C::NSTAGE - 1 < cnt;
-      tile_step<C>(a, smem + ((i + C::NSTAGE - 1) % C::NSTAGE) * C::TILE_BYTES, smem + st * C::TILE_BYTES, p_s,
-                   alpha_s, flag_s, issue, b, k0 + i + C::NSTAGE - 1, (k0 + i) * C::TILE, vis, i, wave, lane,
-                   s_base, v_base, qf, m_run, l_run, O);
-    }
+      tile_step<C>(a, smem + ((i + C::NSTAGE - 1) % C::NSTAGE) * C::TILE_BYTES, smem + (i % C::NSTAGE) * C::TILE_BYTES,
+                   p_s, smem + C::OFF_Q + wave * 4096, alpha_s, flag_s, i + C::NSTAGE - 1 < cnt, b,
+                   k0 + i + C::NSTAGE - 1, (k0 + i) * C::TILE, vis, i, wave, lane, dma_off, s_base, tr_base, qf, m_run,
+                   l_run, O);
+    };
+    // tile 0 is peeled: the compiler's wait for the q registers then lands
+    // in front of its first use (leaving the DMA of tile 1 in flight)
+    // instead of in front of the loop
+    step(0);
+    for (int i = 1; i < cnt; ++i) step(i);
 
     // ---- finalise the segment ----------------------------------------
-#pragma unroll
-    for (int ht = 0; ht < C::HTW; ++ht) {
-      const int hl = (wave * C::HTW + ht) * 16 + l16;
-      if (g == 0) {
-        m_s[hl] = m_run[ht];
-        l_s[hl] = l_run[ht];
-      }
+    o_settle<T>(O);
+    if (hi == 0) {
+      m_s[wave * 32 + l32] = m_run;
+      l_s[wave * 32 + l32] = l_run;
     }
     lds_barrier();
     const int pid = w + u;  // partial slot of this (work-group, stream) piece
+    {
+      // this lane's O elements: head ht*32 + 8*q4 + 4*hi + rr, column
+      // wave*CPW + ct*32 + l32; one base pointer, compile-time offsets
+      float* base = whole ? a.o_lat + ((size_t)v * a.H + h_base) * C::DL : a.part_o + (size_t)pid * C::HP * C::DL;
+      base += (size_t)(4 * hi) * C::DL + wave * C::CPW + l32;
 #pragma unroll
-    for (int ht = 0; ht < C::NHT; ++ht) {
-      const float4 l4 = *reinterpret_cast<const float4*>(l_s + ht * 16 + 4 * g);
-      const float inv[4] = {1.f / l4.x, 1.f / l4.y, 1.f / l4.z, 1.f / l4.w};
+      for (int ht = 0; ht < C::NTH; ++ht) {
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int hl = ht * 16 + 4 * g + ii;
-        if (h_base + hl >= a.H) continue;
-        float* dst = whole ? a.o_lat + ((size_t)v * a.H + h_base + hl) * C::DL
-                           : a.part_o + ((size_t)pid * C::HP + hl) * C::DL;
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 l4 = *reinterpret_cast<const float4*>(l_s + ht * 32 + 8 * q4 + 4 * hi);
+          const float inv[4] = {1.f / l4.x, 1.f / l4.y, 1.f / l4.z, 1.f / l4.w};
 #pragma unroll
-        for (int ct = 0; ct < C::NCT; ++ct) dst[wave * C::CPW + ct * 16 + l16] = O[ht][ct][ii] * inv[ii];
+          for (int rr = 0; rr < 4; ++rr) {
+            const int hl0 = ht * 32 + 8 * q4 + rr;
+            if (h_base + hl0 + 4 * hi >= a.H) continue;
+#pragma unroll
+            for (int ct = 0; ct < C::NCT; ++ct) base[hl0 * C::DL + ct * 32] = O[ht][ct][4 * q4 + rr] * inv[rr];
+          }
+        }
       }
     }
-#pragma unroll
-    for (int ht = 0; ht < C::HTW; ++ht) {
-      const int hl = (wave * C::HTW + ht) * 16 + l16;
-      if (g == 0 && h_base + hl < a.H) {
-        const float lse2 = m_run[ht] + __log2f(l_run[ht]);
+    {
+      const int hl = wave * 32 + l32;
+      if (hi == 0 && h_base + hl < a.H) {
+        const float lse2 = m_run + __log2f(l_run);
         if (whole) {
           if (a.lse) a.lse[(size_t)v * a.H + h_base + hl] = lse2 * 0.69314718055994531f;
         } else {
@@ -453,61 +636,177 @@ __global__ __launch_bounds__(C::NTHR, 1) void attn_split_kernel(AttnArgs a) {
     }
     lds_barrier();
     gcur = tb0 + k1;
-    ++u;
   }
 }
 
-// Prefix sum of 32-token tiles over the streams u = v * n_hg + head group
-// (one block).  Invalid lengths get no tiles and raise error bit 4.
-__global__ __launch_bounds__(1024) void attn_plan_kernel(const int32_t* __restrict__ kv_len, int n_q, int n_hg, int U,
-                                                        int cap, int32_t* __restrict__ tile_off,
-                                                        int32_t* __restrict__ err, const int32_t* __restrict__ table,
-                                                        int page_size, int max_pages, int n_pages) {
-  __shared__ int buf[1024];
-  __shared__ int carry;
-  const int tid = threadIdx.x;
-  // page ids the split kernel will follow must lie inside the pool (it
-  // reads zeros instead of a bad page; this raises error bit 2)
-  if (table) {
-    const int B = U / (n_hg * n_q);
-    for (long i = tid; i < (long)B * max_pages; i += 1024) {
-      const int b = (int)(i / max_pages), p = (int)(i % max_pages);
-      const int L = kv_len[b];
-      if (L >= n_q && L <= cap && p < (L + page_size - 1) / page_size) {
-        const int pg = table[i];
-        if (pg < 0 || pg >= n_pages) atomicOr(err, 2);
-      }
-    }
+constexpr int kPlanThreads = 256;
+
+// Inclusive prefix sum over the plan block (4 waves); *total gets the sum.
+__device__ inline int plan_scan(int v, int* wsum, int* total) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(v, off, 64);
+    if (lane >= off) v += y;
   }
-  if (tid == 0) carry = 0;
+  if (lane == 63) wsum[wv] = v;
   __syncthreads();
-  for (int base = 0; base < U; base += 1024) {
-    const int u = base + tid;
-    int cnt = 0;
-    if (u < U) {
-      const int v = u / n_hg;
-      const int b = v / n_q, j = v - b * n_q;
-      const int L = kv_len[b];
-      if (L < n_q || L > cap) {
-        if (j == 0 && u % n_hg == 0) atomicOr(err, 4);
-      } else {
-        cnt = (L - n_q + j + 1 + 31) / 32;
+  int pre = 0, tot = 0;
+#pragma unroll
+  for (int k = 0; k < kPlanThreads / 64; ++k) {
+    pre += k < wv ? wsum[k] : 0;
+    tot += wsum[k];
+  }
+  __syncthreads();
+  *total = tot;
+  return v + pre;
+}
+
+__device__ inline int plan_max(int v, int* wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = max(v, __shfl_xor(v, off, 64));
+  if (lane == 0) wsum[wv] = v;
+  __syncthreads();
+  int m = wsum[0];
+#pragma unroll
+  for (int k = 1; k < kPlanThreads / 64; ++k) m = max(m, wsum[k]);
+  __syncthreads();
+  return m;
+}
+
+// Work plan (one block).  Streams u = v * n_hg + head group are cut into
+// 32-token tiles; every work-group gets a contiguous range of the
+// concatenated tile list.  Two ways to cut it:
+//   * even: per0 = ceil(T / G) tiles each; ranges may span stream ends, so a
+//     work-group can run several segments (each costs a q load, a pipeline
+//     fill and a 256 KB partial write);
+//   * aligned: every stream is cut into chunks of `per` tiles, per the
+//     smallest value tried that yields at most G chunks; one segment per
+//     work-group.
+// The cheaper one under (tiles + 3 x segments) on the busiest work-group is
+// used.  Outputs: srec[u] = {first tile, end tile, visible rows, 0},
+// wfl[u] = {first, last work-group} (-1 for an invalid length), wrec[w] =
+// {g0, g1, first stream, its srec}.  Invalid lengths get no tiles and raise
+// error bit 4; page ids the split kernel will follow must lie inside the
+// pool (error bit 2; the split kernel reads zeros instead).
+__global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnArgs a, int cap) {
+  __shared__ int wsum[kPlanThreads / 64];
+  __shared__ int hist[1024];
+  __shared__ int cand[8];
+  const int tid = threadIdx.x;
+  const int U = a.U, G = a.G, n_q = a.n_q, n_hg = a.n_hg;
+  if (a.paged) {
+    for (long i = tid; i < (long)a.B * a.max_pages; i += kPlanThreads) {
+      const int b = (int)(i / a.max_pages), p = (int)(i % a.max_pages);
+      const int L = a.kv_len[b];
+      if (L >= n_q && L <= cap && p < (L + a.page_size - 1) / a.page_size) {
+        const int pg = a.page_table[i];
+        if (pg < 0 || pg >= a.n_pages) atomicOr(a.err, 2);
       }
     }
-    buf[tid] = cnt;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-      const int add = tid >= off ? buf[tid - off] : 0;
-      __syncthreads();
-      buf[tid] += add;
-      __syncthreads();
-    }
-    if (u < U) tile_off[u] = carry + buf[tid] - cnt;
-    __syncthreads();
-    if (tid == 1023) carry += buf[1023];
-    __syncthreads();
   }
-  if (tid == 0) tile_off[U] = carry;
+  // tile prefix sums and per-stream records
+  int carry = 0, nz = 0;
+  for (int base = 0; base < U; base += kPlanThreads) {
+    const int u = base + tid;
+    int cnt = 0, vis = 0;
+    if (u < U) {
+      const int v = u / n_hg, b = v / n_q, j = v - b * n_q;
+      const int L = a.kv_len[b];
+      if (L < n_q || L > cap) {
+        if (j == 0 && u % n_hg == 0) atomicOr(a.err, 4);
+      } else {
+        vis = L - n_q + j + 1;
+        cnt = (vis + 31) / 32;
+      }
+    }
+    int tot, tot_nz;
+    const int inc = plan_scan(cnt, wsum, &tot);
+    plan_scan(cnt > 0, wsum, &tot_nz);
+    if (u < U) reinterpret_cast<int4*>(a.srec)[u] = make_int4(carry + inc - cnt, carry + inc, vis, 0);
+    carry += tot;
+    nz += tot_nz;
+  }
+  const int T = carry;
+  const int per0 = max(1, (T + G - 1) / G);
+  for (int w = tid; w < G; w += kPlanThreads) hist[w] = 0;
+  if (tid < 8) cand[tid] = 0;
+  __syncthreads();  // srec visible to the whole block
+
+  // even cut: streams starting strictly inside a work-group's range add a
+  // segment to it; aligned cut: chunk counts for per0 .. per0 + 7
+  int csum[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int u = tid; u < U; u += kPlanThreads) {
+    const int4 r = reinterpret_cast<const int4*>(a.srec)[u];
+    if (r.y > r.x) {
+      if (r.x % per0) atomicAdd(&hist[r.x / per0], 1);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) csum[c] += (r.y - r.x + per0 + c - 1) / (per0 + c);
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    int x = csum[c];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+    if ((tid & 63) == 0) atomicAdd(&cand[c], x);
+  }
+  __syncthreads();
+  int hmax = 0;
+  for (int w = tid; w < G; w += kPlanThreads) hmax = max(hmax, hist[w]);
+  const int smax = 1 + plan_max(hmax, wsum);
+  int per = 0;
+  for (int c = 7; c >= 0; --c)
+    if (cand[c] <= G) per = per0 + c;
+  if (per == 0 && G > nz) per = (T + (G - nz) - 1) / (G - nz);  // T/per + nz chunks at most
+  const bool aligned = per > 0 && (per + 3 <= per0 + 3 * smax);
+
+  // work-group records
+  for (int w = tid; w < G; w += kPlanThreads) {
+    int* wr = a.wrec + 8 * w;
+    int g0 = 0, g1 = 0, u0 = 0;
+    int4 r = make_int4(0, 0, 0, 0);
+    if (!aligned && w * per0 < T) {
+      g0 = w * per0;
+      g1 = min(g0 + per0, T);
+      int lo = 0, hi = U;  // last stream with start <= g0 (and tiles)
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (reinterpret_cast<const int4*>(a.srec)[mid].x <= g0) lo = mid; else hi = mid;
+      }
+      u0 = lo;
+      r = reinterpret_cast<const int4*>(a.srec)[u0];
+      while (r.y <= g0) r = reinterpret_cast<const int4*>(a.srec)[++u0];  // skip empty streams
+    }
+    wr[0] = g0; wr[1] = g1; wr[2] = u0; wr[3] = r.x; wr[4] = r.y; wr[5] = r.z; wr[6] = 0; wr[7] = 0;
+  }
+  __syncthreads();
+  int chunk_base = 0;
+  for (int base = 0; base < U; base += kPlanThreads) {
+    const int u = base + tid;
+    const int4 r = u < U ? reinterpret_cast<const int4*>(a.srec)[u] : make_int4(0, 0, 0, 0);
+    const int nch = aligned ? (r.y - r.x + per - 1) / per : 0;
+    int tot;
+    const int c0 = chunk_base + plan_scan(nch, wsum, &tot) - nch;
+    chunk_base += tot;
+    if (u < U) {
+      int2 f = make_int2(-1, -1);
+      if (r.y > r.x) {
+        if (aligned) {
+          f = make_int2(c0, c0 + nch - 1);
+          for (int c = 0; c < nch; ++c) {
+            int* wr = a.wrec + 8 * (c0 + c);
+            wr[0] = r.x + c * per; wr[1] = min(r.x + (c + 1) * per, r.y); wr[2] = u;
+            wr[3] = r.x; wr[4] = r.y; wr[5] = r.z;
+          }
+        } else {
+          f = make_int2(r.x / per0, (r.y - 1) / per0);
+        }
+      }
+      reinterpret_cast<int2*>(a.wfl)[u] = f;
+    }
+  }
 }
 
 // Log-sum-exp merge of the pieces of every stream that was cut by a
@@ -527,18 +826,15 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   const int h = hgrp * HP + hl;                    // global head
   const int c0 = (tid % TPH) * 4;
   const bool active = (hl < HP) && (h < a.H);
-  const int G = a.G;
-  const int Ttot = a.tile_off[a.U];
-  const int per = (Ttot + G - 1) / G;
-  const int t0 = a.tile_off[u], t1 = a.tile_off[u + 1];
-  if (t1 == t0) {  // invalid length: flagged by the plan kernel; poison the output
+  const int2 fl = reinterpret_cast<const int2*>(a.wfl)[u];
+  const int wf = fl.x, wl = fl.y;
+  if (wf < 0) {  // invalid length: flagged by the plan kernel; poison the output
     if (active) {
       *reinterpret_cast<float4*>(a.o_lat + ((size_t)v * a.H + h) * DL + c0) = make_float4(NAN, NAN, NAN, NAN);
       if (a.lse && c0 == 0) a.lse[(size_t)v * a.H + h] = NAN;
     }
     return;
   }
-  const int wf = t0 / per, wl = (t1 - 1) / per;
   if (wf == wl) return;  // written whole by the split kernel
   const int n = wl - wf + 1;
   if (tid % TPH == 0 && active) {
@@ -576,6 +872,8 @@ int attn_head_group(bool bf16) { return bf16 ? CfgBf16::HP : CfgF32::HP; }
 
 int attn_tile() { return 32; }
 
+size_t attn_sched_ints(int U, int G) { return 6 * (size_t)U + 8 * (size_t)G; }
+
 template <class C>
 static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t s) {
   static bool attr_set = false;
@@ -586,8 +884,7 @@ static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t s) {
     attr_set = true;
   }
   const int cap = a.paged ? a.max_pages * a.page_size : a.s_max;
-  hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(1024), 0, s, a.kv_len, a.n_q, a.n_hg, a.U, cap, a.tile_off,
-                     a.err, a.paged ? a.page_table : nullptr, a.page_size, a.max_pages, a.n_pages);
+  hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, a, cap);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_split_kernel<C>, dim3(a.G), dim3(C::NTHR), C::LDS_BYTES, s, a);
@@ -602,6 +899,11 @@ hipError_t launch_attention(const AttnArgs& a_in, bool bf16, hipStream_t s) {
   AttnArgs a = a_in;
   a.n_hg = (a.H + attn_head_group(bf16) - 1) / attn_head_group(bf16);
   a.U = a.V * a.n_hg;
+  if (a.G < 8 || a.G > 1024) return hipErrorInvalidValue;
+  // plan storage: wrec [8G] | srec [4U] | wfl [2U]
+  a.wrec = a.sched;
+  a.srec = a.wrec + 8 * a.G;
+  a.wfl = a.srec + 4 * a.U;
   return bf16 ? launch_attn_t<CfgBf16>(a, s) : launch_attn_t<CfgF32>(a, s);
 }
 

@@ -71,10 +71,14 @@ struct AttnArgs {
   const int32_t* kv_len;
   int B, n_q, H, V;
   int n_hg, U;                 // head groups per query row; streams U = V * n_hg (set by the launcher)
-  int32_t* tile_off;           // [U+1]  (written by the plan kernel)
+  // work plan (written by the plan kernel), carved out of `sched`:
+  int32_t* sched;              // plan storage, attn_sched_ints(U, G) ints
+  int32_t* wrec;               // [G][8] {g0, g1, first stream u, srec[u] (3), 0, 0}
+  int32_t* srec;               // [U][4] {first tile, end tile, visible rows, 0}
+  int32_t* wfl;                // [U][2] first / last work-group of stream u (-1: invalid length)
   float* o_lat;                // [V][H][d_latent]
   float* lse;                  // [V][H] natural-log LSE of scaled scores, or null
-  float* part_o;               // [(G+U)][head group][d_latent]
+  float* part_o;               // [(G+U)][head group][d_latent], slot w + u
   float* part_lse;             // [(G+U)][head group]
   int32_t* err;
   float scale_log2;            // softmax scale * log2(e)
@@ -84,6 +88,7 @@ struct AttnArgs {
 int attn_supported(bool bf16, int H, int d_latent, int d_rope);
 int attn_head_group(bool bf16);  // heads per attention work-group
 int attn_tile();
+size_t attn_sched_ints(int U, int G);  // ints of plan storage for U streams, G work-groups
 hipError_t launch_attention(const AttnArgs& a, bool bf16, hipStream_t s);
 
 }  // namespace mla
