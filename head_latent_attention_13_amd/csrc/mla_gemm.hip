@@ -138,9 +138,21 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     wp[ni] = reinterpret_cast<const T*>(g.Wp) + (size_t)nt * FR + lane * KPL;
   }
 
+  // Weights are read exactly once.  With fp32 activations (the output
+  // projection: its A operand is re-read by every column block) the weight
+  // stream uses non-temporal loads so that it does not evict A from L2.
+  constexpr bool kStreamW = sizeof(TA) == 4 && sizeof(frag) == 16;
   auto load_b = [&](frag (&b)[NT], int kb) {
 #pragma unroll
-    for (int ni = 0; ni < NT; ++ni) b[ni] = *reinterpret_cast<const frag*>(wp[ni] + (size_t)kb * kb_stride);
+    for (int ni = 0; ni < NT; ++ni) {
+      if constexpr (kStreamW) {
+        typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+        b[ni] = __builtin_bit_cast(
+            frag, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(wp[ni] + (size_t)kb * kb_stride)));
+      } else {
+        b[ni] = *reinterpret_cast<const frag*>(wp[ni] + (size_t)kb * kb_stride);
+      }
+    }
   };
   auto load_a = [&](frag (&a)[MT], int kb) {
 #pragma unroll
@@ -159,18 +171,37 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int ni = 0; ni < NT; ++ni) acc[mi][ni] = F::mma(a[mi], b[ni], acc[mi][ni]);
   };
-  // U k-blocks per step: all their loads are issued before the first MFMA
-  constexpr int U = (32 / NT) > 1 ? (32 / NT) : 1;
-  int kb = kb0;
-  for (; kb + U <= kb1; kb += U) {
-    frag b[U][NT], a[U][MT];
+  // Software pipeline over groups of U k-blocks with two register buffers:
+  // the loads of group i+1 are issued before the MFMAs of group i, so the
+  // weight stream never drains between groups.
+  constexpr int U = (12 / (NT + MT)) > 1 ? (12 / (NT + MT)) : 1;
+  auto load_group = [&](frag (&b)[U][NT], frag (&a)[U][MT], int kb) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       load_b(b[u], kb + u);
       load_a(a[u], kb + u);
     }
+  };
+  auto mma_group = [&](const frag (&b)[U][NT], const frag (&a)[U][MT]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) mma_all(a[u], b[u]);
+  };
+  int kb = kb0;
+  if (kb + U <= kb1) {
+    frag b0[U][NT], a0[U][MT], b1[U][NT], a1[U][MT];
+    load_group(b0, a0, kb);
+    for (;;) {
+      const bool n1 = kb + 2 * U <= kb1;
+      if (n1) load_group(b1, a1, kb + U);
+      mma_group(b0, a0);
+      kb += U;
+      if (!n1) break;
+      const bool n2 = kb + 2 * U <= kb1;
+      if (n2) load_group(b0, a0, kb + U);
+      mma_group(b1, a1);
+      kb += U;
+      if (!n2) break;
+    }
   }
   for (; kb < kb1; ++kb) {
     frag b[NT], a[MT];
