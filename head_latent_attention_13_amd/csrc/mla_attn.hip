@@ -681,9 +681,9 @@ __device__ inline int plan_max(int v, int* wsum) {
 //   * even: per0 = ceil(T / G) tiles each; ranges may span stream ends, so a
 //     work-group can run several segments (each costs a q load, a pipeline
 //     fill and a 256 KB partial write);
-//   * aligned: every stream is cut into chunks of `per` tiles, per the
-//     smallest value tried that yields at most G chunks; one segment per
-//     work-group.
+//   * aligned: every stream is cut into chunks of `per` tiles with
+//     per = max(per0, ceil(T / (G - nz))) (nz: streams with tiles), which
+//     gives at most T / per + nz <= G chunks; one segment per work-group.
 // The cheaper one under (tiles + 3 x segments) on the busiest work-group is
 // used.  Outputs: srec[u] = {first tile, end tile, visible rows, 0},
 // wfl[u] = {first, last work-group} (-1 for an invalid length), wrec[w] =
@@ -691,11 +691,18 @@ __device__ inline int plan_max(int v, int* wsum) {
 // error bit 4; page ids the split kernel will follow must lie inside the
 // pool (error bit 2; the split kernel reads zeros instead).
 __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnArgs a, int cap) {
+  constexpr int kLdsU = 2048;  // stream records staged in LDS up to this many streams
   __shared__ int wsum[kPlanThreads / 64];
   __shared__ int hist[1024];
-  __shared__ int cand[8];
+  __shared__ int sx[kLdsU], sy[kLdsU];
   const int tid = threadIdx.x;
   const int U = a.U, G = a.G, n_q = a.n_q, n_hg = a.n_hg;
+  const bool staged = U <= kLdsU;
+  auto rec = [&](int u) -> int2 {
+    if (staged) return make_int2(sx[u], sy[u]);
+    const int4 r = reinterpret_cast<const int4*>(a.srec)[u];
+    return make_int2(r.x, r.y);
+  };
   if (a.paged) {
     for (long i = tid; i < (long)a.B * a.max_pages; i += kPlanThreads) {
       const int b = (int)(i / a.max_pages), p = (int)(i % a.max_pages);
@@ -724,42 +731,33 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnArgs a, int
     int tot, tot_nz;
     const int inc = plan_scan(cnt, wsum, &tot);
     plan_scan(cnt > 0, wsum, &tot_nz);
-    if (u < U) reinterpret_cast<int4*>(a.srec)[u] = make_int4(carry + inc - cnt, carry + inc, vis, 0);
+    if (u < U) {
+      reinterpret_cast<int4*>(a.srec)[u] = make_int4(carry + inc - cnt, carry + inc, vis, 0);
+      if (staged) {
+        sx[u] = carry + inc - cnt;
+        sy[u] = carry + inc;
+      }
+    }
     carry += tot;
     nz += tot_nz;
   }
   const int T = carry;
   const int per0 = max(1, (T + G - 1) / G);
   for (int w = tid; w < G; w += kPlanThreads) hist[w] = 0;
-  if (tid < 8) cand[tid] = 0;
   __syncthreads();  // srec visible to the whole block
 
   // even cut: streams starting strictly inside a work-group's range add a
   // segment to it; aligned cut: chunk counts for per0 .. per0 + 7
-  int csum[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   for (int u = tid; u < U; u += kPlanThreads) {
-    const int4 r = reinterpret_cast<const int4*>(a.srec)[u];
-    if (r.y > r.x) {
-      if (r.x % per0) atomicAdd(&hist[r.x / per0], 1);
-#pragma unroll
-      for (int c = 0; c < 8; ++c) csum[c] += (r.y - r.x + per0 + c - 1) / (per0 + c);
-    }
-  }
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    int x = csum[c];
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
-    if ((tid & 63) == 0) atomicAdd(&cand[c], x);
+    const int2 r = rec(u);
+    if (r.y > r.x && r.x % per0) atomicAdd(&hist[r.x / per0], 1);
   }
   __syncthreads();
   int hmax = 0;
   for (int w = tid; w < G; w += kPlanThreads) hmax = max(hmax, hist[w]);
   const int smax = 1 + plan_max(hmax, wsum);
-  int per = 0;
-  for (int c = 7; c >= 0; --c)
-    if (cand[c] <= G) per = per0 + c;
-  if (per == 0 && G > nz) per = (T + (G - nz) - 1) / (G - nz);  // T/per + nz chunks at most
+  // chunks(per) <= T / per + nz, so this per yields at most G chunks
+  const int per = G > nz ? max(per0, (T + (G - nz) - 1) / (G - nz)) : 0;
   const bool aligned = per > 0 && (per + 3 <= per0 + 3 * smax);
 
   // work-group records
@@ -773,11 +771,11 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnArgs a, int
       int lo = 0, hi = U;  // last stream with start <= g0 (and tiles)
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
-        if (reinterpret_cast<const int4*>(a.srec)[mid].x <= g0) lo = mid; else hi = mid;
+        if (rec(mid).x <= g0) lo = mid; else hi = mid;
       }
       u0 = lo;
+      while (rec(u0).y <= g0) ++u0;  // skip empty streams
       r = reinterpret_cast<const int4*>(a.srec)[u0];
-      while (r.y <= g0) r = reinterpret_cast<const int4*>(a.srec)[++u0];  // skip empty streams
     }
     wr[0] = g0; wr[1] = g1; wr[2] = u0; wr[3] = r.x; wr[4] = r.y; wr[5] = r.z; wr[6] = 0; wr[7] = 0;
   }
@@ -785,7 +783,11 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnArgs a, int
   int chunk_base = 0;
   for (int base = 0; base < U; base += kPlanThreads) {
     const int u = base + tid;
-    const int4 r = u < U ? reinterpret_cast<const int4*>(a.srec)[u] : make_int4(0, 0, 0, 0);
+    int4 r = make_int4(0, 0, 0, 0);
+    if (u < U) {
+      const int2 xy = rec(u);
+      r = make_int4(xy.x, xy.y, 0, 0);
+    }
     const int nch = aligned ? (r.y - r.x + per - 1) / per : 0;
     int tot;
     const int c0 = chunk_base + plan_scan(nch, wsum, &tot) - nch;
@@ -795,10 +797,11 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnArgs a, int
       if (r.y > r.x) {
         if (aligned) {
           f = make_int2(c0, c0 + nch - 1);
+          const int vis = reinterpret_cast<const int4*>(a.srec)[u].z;
           for (int c = 0; c < nch; ++c) {
             int* wr = a.wrec + 8 * (c0 + c);
             wr[0] = r.x + c * per; wr[1] = min(r.x + (c + 1) * per, r.y); wr[2] = u;
-            wr[3] = r.x; wr[4] = r.y; wr[5] = r.z;
+            wr[3] = r.x; wr[4] = r.y; wr[5] = vis;
           }
         } else {
           f = make_int2(r.x / per0, (r.y - 1) / per0);
@@ -814,53 +817,72 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnArgs a, int
 // Block = (stream, HPB heads of its group); each thread owns 4 columns.
 template <int HP, int DL>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
-  constexpr int TPH = DL / 4;                      // threads per head
-  constexpr int HPB = 256 / TPH;                   // heads per block
-  constexpr int MAXS = 32;
-  __shared__ float wts[HPB][MAXS];
-  __shared__ float lse_s[HPB];
+  constexpr int TPH = DL / 4;  // threads per head (4 columns each)
+  constexpr int HPB = 256 / TPH;  // heads per block
+  constexpr int CH = 16;          // pieces whose O values are held in registers at once
   const int u = blockIdx.x, tid = threadIdx.x;
   const int v = u / a.n_hg, hgrp = u - v * a.n_hg;
-  const int r = tid / TPH;                         // head slot in the block
-  const int hl = blockIdx.y * HPB + r;             // head within the group
-  const int h = hgrp * HP + hl;                    // global head
+  const int hl = blockIdx.y * HPB + tid / TPH;  // head within the group
+  const int h = hgrp * HP + hl;                 // global head
   const int c0 = (tid % TPH) * 4;
-  const bool active = (hl < HP) && (h < a.H);
+  if (hl >= HP || h >= a.H) return;
   const int2 fl = reinterpret_cast<const int2*>(a.wfl)[u];
   const int wf = fl.x, wl = fl.y;
+  float* dst = a.o_lat + ((size_t)v * a.H + h) * DL + c0;
   if (wf < 0) {  // invalid length: flagged by the plan kernel; poison the output
-    if (active) {
-      *reinterpret_cast<float4*>(a.o_lat + ((size_t)v * a.H + h) * DL + c0) = make_float4(NAN, NAN, NAN, NAN);
-      if (a.lse && c0 == 0) a.lse[(size_t)v * a.H + h] = NAN;
-    }
+    *reinterpret_cast<float4*>(dst) = make_float4(NAN, NAN, NAN, NAN);
+    if (a.lse && c0 == 0) a.lse[(size_t)v * a.H + h] = NAN;
     return;
   }
   if (wf == wl) return;  // written whole by the split kernel
   const int n = wl - wf + 1;
-  if (tid % TPH == 0 && active) {
-    const float* pl = a.part_lse + (size_t)(wf + u) * HP + hl;   // piece s at pl[s * HP]
-    float mx = -INFINITY;
-    for (int s = 0; s < n; ++s) mx = fmaxf(mx, pl[(size_t)s * HP]);
-    float sum = 0.f;
-    for (int s = 0; s < n; ++s) sum += exp2f(pl[(size_t)s * HP] - mx);
-    const float L = mx + log2f(sum);
-    lse_s[r] = L;
-    for (int s = 0; s < n && s < MAXS; ++s) wts[r][s] = exp2f(pl[(size_t)s * HP] - L);
-    if (a.lse) a.lse[(size_t)v * a.H + h] = L * 0.69314718055994531f;
-  }
-  __syncthreads();
-  if (!active) return;
+  const float* pl = a.part_lse + (size_t)(wf + u) * HP + hl;             // piece s at pl[s * HP]
   const float* src = a.part_o + ((size_t)(wf + u) * HP + hl) * DL + c0;  // piece s at src[s * HP * DL]
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s = 0; s < n; ++s) {
-    const float wgt = (s < MAXS) ? wts[r][s] : exp2f(a.part_lse[(size_t)(wf + s + u) * HP + hl] - lse_s[r]);
-    const float4 x = *reinterpret_cast<const float4*>(src + (size_t)s * HP * DL);
-    acc.x += wgt * x.x;
-    acc.y += wgt * x.y;
-    acc.z += wgt * x.z;
-    acc.w += wgt * x.w;
+  // Loads are issued CH pieces at a time (O values and LSEs together), so a
+  // chunk costs one memory round trip.  Pass 1 forms the total LSE with a
+  // running max; pass 2 weights the O values (the first chunk stays in
+  // registers from pass 1).
+  float4 x[CH];
+  float lv[CH];
+  auto load_chunk = [&](int base, bool with_o) {
+#pragma unroll
+    for (int s = 0; s < CH; ++s) {
+      const int p = min(base + s, n - 1);  // clamped: lanes past n reload the last piece
+      lv[s] = pl[(size_t)p * HP];
+      if (with_o) x[s] = *reinterpret_cast<const float4*>(src + (size_t)p * HP * DL);
+    }
+  };
+  load_chunk(0, true);
+  float mx = -INFINITY, sum = 0.f;
+  for (int base = 0; base < n; base += CH) {
+    if (base > 0) load_chunk(base, false);
+    float cm = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < CH; ++s) cm = fmaxf(cm, lv[s]);  // clamped entries repeat a real one
+    const float nm = fmaxf(mx, cm);
+    float cs = 0.f;
+#pragma unroll
+    for (int s = 0; s < CH; ++s) cs += (base + s < n) ? exp2f(lv[s] - nm) : 0.f;
+    sum = sum * exp2f(mx - nm) + cs;
+    mx = nm;
   }
-  *reinterpret_cast<float4*>(a.o_lat + ((size_t)v * a.H + h) * DL + c0) = acc;
+  const float L = mx + log2f(sum);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int base = 0; base < n; base += CH) {
+    if (base > 0 || n > CH) load_chunk(base, true);
+#pragma unroll
+    for (int s = 0; s < CH; ++s) {
+      if (base + s < n) {
+        const float wgt = exp2f(lv[s] - L);
+        acc.x += wgt * x[s].x;
+        acc.y += wgt * x[s].y;
+        acc.z += wgt * x[s].z;
+        acc.w += wgt * x[s].w;
+      }
+    }
+  }
+  *reinterpret_cast<float4*>(dst) = acc;
+  if (a.lse && c0 == 0) a.lse[(size_t)v * a.H + h] = L * 0.69314718055994531f;
 }
 
 int attn_supported(bool bf16, int H, int d_latent, int d_rope) {
