@@ -251,11 +251,22 @@ __global__ __launch_bounds__(256) void splitk_epilogue_kernel(GemmArgs g) {
   if (idx >= (long)g.e.M * pairs) return;
   const int m = (int)(idx / pairs);
   const int n = (int)(idx % pairs) * 2;
+  // slices are loaded CH at a time (one memory round trip per chunk) and
+  // summed in slice order
+  constexpr int CH = 8;
   float v0 = 0.f, v1 = 0.f;
-  for (int ks = 0; ks < g.ksplit; ++ks) {
-    const float2 p = *reinterpret_cast<const float2*>(g.part + ((size_t)ks * g.e.M + m) * g.Np + n);
-    v0 += p.x;
-    v1 += p.y;
+  for (int base = 0; base < g.ksplit; base += CH) {
+    float2 p[CH];
+#pragma unroll
+    for (int j = 0; j < CH; ++j)
+      p[j] = *reinterpret_cast<const float2*>(g.part + ((size_t)min(base + j, g.ksplit - 1) * g.e.M + m) * g.Np + n);
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      if (base + j < g.ksplit) {
+        v0 += p[j].x;
+        v1 += p[j].y;
+      }
+    }
   }
   epi_pair<T>(g.e, m, n, v0, v1);
 }
