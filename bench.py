@@ -66,14 +66,16 @@ def measured_traffic(call: str):
 
 
 def copy_calibration(mb: int, steps: int):
+    """A plain streaming kernel of known traffic (reads and writes mb MiB per
+    launch) for scaling the HBM byte counters."""
     import torch
     n = mb * (1 << 20) // 4
     a = torch.ones(n, device="cuda")
     b = torch.empty_like(a)
     for _ in range(steps):
-        b.copy_(a)
+        torch.add(a, 1.0, out=b)
     torch.cuda.synchronize()
-    print(json.dumps({"copy_calibration_bytes_read": n * 4, "launches": steps}))
+    print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4, "launches": steps}))
 
 
 def cpu_baseline(case, n_budget_s: float):

@@ -1,0 +1,165 @@
+#!/usr/bin/env python3
+"""Profiles one bench.py workload with rocprofv3 and writes the summaries
+that bench.py and the documentation use.
+
+Runs, each as its own rocprofv3 process with the program directly after
+``--`` (this script itself never touches the GPU):
+  1. ``--kernel-trace --stats`` over a short bench run (per-kernel durations);
+  2. ``--pmc FETCH_SIZE`` and 3. ``--pmc WRITE_SIZE`` over a 3-step bench run;
+  4./5. the same two counters over a plain device copy of known size
+     (``bench.py --copy-calib-mb``), which calibrates the counters to bytes.
+
+Writes profiles/kernel_stats_<workload>.txt, profiles/hbm_traffic_<workload>.txt
+and, for the default workload, profiles/hbm_traffic.txt (JSON read by
+bench.py: HBM bytes per call, tagged with a hash of the kernel sources).
+
+    python bench_counters.py [--config 1] [--out gpurun_out/counters]
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import json
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CALLS = ("mla_compress_append", "mla_q_proj", "mla_attention", "mla_out_proj")
+# kernels each call launches, in order (split-K GEMMs add an epilogue kernel)
+CALL_OF_POSITION = ("mla_compress_append", "mla_compress_append", "mla_q_proj", "mla_q_proj", "mla_q_proj",
+                    "mla_attention", "mla_attention", "mla_attention", "mla_out_proj", "mla_out_proj")
+COPY_MB = 512
+
+
+def run(cmd, out_dir, name, timeout):
+    log = os.path.join(out_dir, name + ".log")
+    print("[counters] " + " ".join(cmd), flush=True)
+    with open(log, "w") as f:
+        r = subprocess.run(cmd, stdout=f, stderr=subprocess.STDOUT, timeout=timeout, cwd="/tmp",
+                           env=dict(os.environ, TMPDIR="/tmp"))
+    print(f"[counters] {name}: exit {r.returncode}", flush=True)
+    if r.returncode != 0:
+        with open(log) as f:
+            sys.stdout.write(f.read()[-3000:])
+        raise SystemExit(r.returncode)
+
+
+def find(out_dir, name, suffix):
+    hits = glob.glob(os.path.join(out_dir, name, "**", "*" + suffix), recursive=True)
+    if not hits:
+        raise SystemExit(f"no {suffix} under {out_dir}/{name}")
+    return hits[0]
+
+
+def mla_kernel(name: str) -> bool:
+    return name.startswith("_ZN3mla") or "mla::" in name
+
+
+def counter_per_dispatch(path):
+    """{dispatch id: (kernel name, summed counter value)}"""
+    out = {}
+    with open(path) as f:
+        rd = csv.DictReader(f)
+        need = {"Dispatch_Id", "Kernel_Name", "Counter_Value"}
+        if not need <= set(rd.fieldnames or []):
+            raise SystemExit(f"{path}: columns {rd.fieldnames}")
+        for r in rd:
+            d = int(r["Dispatch_Id"])
+            name, val = r["Kernel_Name"], float(r["Counter_Value"])
+            prev = out.get(d, (name, 0.0))
+            out[d] = (name, prev[1] + val)
+    return out
+
+
+def last_step(per_dispatch):
+    """The 10 dispatches of the last bench step, mapped to their call."""
+    ids = [d for d in sorted(per_dispatch) if mla_kernel(per_dispatch[d][0])]
+    # the breakdown pass ends the run; the absorb kernels come first, so the
+    # last 10 mla dispatches are one whole step
+    step = ids[-len(CALL_OF_POSITION):]
+    return [(CALL_OF_POSITION[i], per_dispatch[d][0], per_dispatch[d][1]) for i, d in enumerate(step)]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "counters"))
+    ap.add_argument("--profiles-dir", default=os.path.join(ROOT, "profiles"))
+    args = ap.parse_args()
+    os.makedirs(args.out, exist_ok=True)
+    py = sys.executable
+    bench = [py, os.path.join(ROOT, "bench.py"), "--config", str(args.config), "--no-cpu-baseline"]
+    stats_cmd = ["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d",
+                 os.path.join(args.out, "trace"), "-o", "run", "--"] + bench + ["--steps", "20", "--warmup", "5"]
+    run(stats_cmd, args.out, "trace", 600)
+    pmc = {}
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        cmd = ["timeout", "-s", "KILL", "120", "rocprofv3", "--pmc", ctr, "--output-format", "csv", "-d",
+               os.path.join(args.out, "pmc_" + ctr), "-o", "run", "--"] + bench + ["--steps", "3", "--warmup", "1"]
+        run(cmd, args.out, "pmc_" + ctr, 180)
+        pmc[ctr] = counter_per_dispatch(find(args.out, "pmc_" + ctr, "counter_collection.csv"))
+        cmd = ["timeout", "-s", "KILL", "60", "rocprofv3", "--pmc", ctr, "--output-format", "csv", "-d",
+               os.path.join(args.out, "copy_" + ctr), "-o", "run", "--", py, os.path.join(ROOT, "bench.py"),
+               "--copy-calib-mb", str(COPY_MB), "--steps", "3"]
+        run(cmd, args.out, "copy_" + ctr, 120)
+        pmc["copy_" + ctr] = counter_per_dispatch(find(args.out, "copy_" + ctr, "counter_collection.csv"))
+
+    # calibration: the copy reads and writes COPY_MB MiB per launch
+    true_bytes = COPY_MB * (1 << 20)
+    factors = {}
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        vals = [v for (n, v) in pmc["copy_" + ctr].values() if "add" in n.lower()]
+        kib = sorted(vals)[len(vals) // 2]
+        factors[ctr] = true_bytes / (kib * 1024.0)
+
+    fetch, write = last_step(pmc["FETCH_SIZE"]), last_step(pmc["WRITE_SIZE"])
+    calls = {c: 0.0 for c in CALLS}
+    rows = []
+    for (call, name, f), (_, _, w) in zip(fetch, write):
+        fb = f * 1024.0 * factors["FETCH_SIZE"]
+        wb = w * 1024.0 * factors["WRITE_SIZE"]
+        calls[call] += fb + wb
+        rows.append((call, name, f, w, fb, wb))
+
+    stats = find(args.out, "trace", "kernel_stats.csv")
+    with open(stats) as f:
+        krows = sorted(csv.DictReader(f), key=lambda r: -float(r["TotalDurationNs"]))
+    sys.path.insert(0, ROOT)
+    from synthetic import config
+    workload = config(args.config).name
+
+    prof = args.profiles_dir
+    os.makedirs(prof, exist_ok=True)
+    with open(os.path.join(prof, f"kernel_stats_{workload}.txt"), "w") as f:
+        f.write(f"# rocprofv3 kernel-trace statistics, workload {workload}\n")
+        f.write("# command (run from /tmp): " + " ".join(stats_cmd).replace(ROOT, ".") + "\n")
+        f.write(f"{'kernel':90s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'total_%':>8s}\n")
+        for r in krows:
+            f.write(f"{r['Name'][:90]:90s} {r['Calls']:>6s} {float(r['AverageNs']) / 1e3:10.2f} "
+                    f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} {float(r['Percentage']):8.2f}\n")
+    with open(os.path.join(prof, f"hbm_traffic_{workload}.txt"), "w") as f:
+        f.write(f"# HBM traffic per dispatch, workload {workload}, last step of a 3-step bench run\n")
+        for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+            f.write(f"# command: timeout -s KILL 120 rocprofv3 --pmc {ctr} --output-format csv -d <dir> -o run -- "
+                    f"python ./bench.py --config {args.config} --no-cpu-baseline --steps 3 --warmup 1\n")
+            f.write(f"# calibration: timeout -s KILL 60 rocprofv3 --pmc {ctr} ... -- python ./bench.py "
+                    f"--copy-calib-mb {COPY_MB} --steps 3 ; factor {factors[ctr]:.4f} bytes per counted byte\n")
+        f.write(f"{'call':22s} {'kernel':70s} {'FETCH_KiB':>12s} {'WRITE_KiB':>12s} {'read_MB':>10s} {'write_MB':>10s}\n")
+        for call, name, fk, wk, fb, wb in rows:
+            f.write(f"{call:22s} {name[:70]:70s} {fk:12.0f} {wk:12.0f} {fb / 1e6:10.2f} {wb / 1e6:10.2f}\n")
+        for c in CALLS:
+            f.write(f"# {c}: {calls[c] / 1e6:.2f} MB per call (read + write)\n")
+    if args.config == 1:
+        import bench
+        out = {"workload": workload, "source_hash": bench.kernel_source_hash(), "factors": factors,
+               "calls": {c: round(v) for c, v in calls.items()}}
+        with open(os.path.join(prof, "hbm_traffic.txt"), "w") as f:
+            json.dump(out, f, indent=1)
+            f.write("\n")
+    print(json.dumps({"factors": factors, "calls_MB": {c: round(v / 1e6, 2) for c, v in calls.items()}}))
+
+
+if __name__ == "__main__":
+    main()
