@@ -157,7 +157,7 @@ enum { G_APP = 0, G_CQ = 1, G_Q = 2, G_OUT = 3 };
 mla_status run_gemm(const WsLayout& W, int which, const GemmPlan& g, bool bf16, bool a_f32, const void* A, int lda,
                     const void* Wp, unsigned char* ws, const EpiArgs& e, hipStream_t s) {
   (void)which;
-  hipError_t err = launch_gemm(g, bf16, a_f32, A, lda, Wp, reinterpret_cast<float*>(ws + W.part), nullptr, e, s);
+  hipError_t err = launch_gemm(g, bf16, a_f32, A, lda, Wp, reinterpret_cast<float*>(ws + W.part), e, s);
   if (err != hipSuccess) return hip_fail(err, "gemm launch");
   return MLA_OK;
 }

@@ -243,6 +243,190 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   }
 }
 
+// --------------------------------------------------------------------------
+// LDS-tiled GEMM for more than 16 rows (batched decode, chunked prefill).
+//
+// Block tile BM x BN = (64 MTW) x (64 NTW); 4 waves in a 2 x 2 grid, wave
+// (wm, wn) computes rows [32 MTW wm, +32 MTW) x columns [32 NTW wn, +32 NTW)
+// with v_mfma_f32_32x32x16_bf16.  A stage covers SKB = 2 k-blocks (64 k):
+//   A: BM rows x 64 k of TA, row-major, 16-byte chunk c of row r stored at
+//      chunk c ^ swz_a(r) (conflict-free 16-lane ds_read_b128 passes);
+//   W: the BN/16 packed 1 KB fragments of each k-block, in fragment order.
+// Both are DMA'd with buffer loads (rows past M and n-tiles past the weight
+// read as zeros) through a 3-stage ring, two stages in flight.
+// A 32x32x16 B operand is read straight from the packed 16-column
+// fragments: lane l takes column tile (l%32)/16, rows 8 (l/32) + 16 ks.
+// --------------------------------------------------------------------------
+template <typename TA, int MTW, int NTW>
+struct TiledCfg {
+  static constexpr int BM = 64 * MTW, BN = 64 * NTW;
+  static constexpr int SKB = 2;                      // k-blocks (32 k) per stage
+  static constexpr int ESA = (int)sizeof(TA);
+  static constexpr int ROWB = SKB * 32 * ESA;        // A bytes per row per stage
+  static constexpr int CPR = ROWB / 16;              // 16-byte chunks per A row
+  static constexpr int A_BYTES = BM * ROWB;
+  static constexpr int NTB = BN / 16;                // packed n-tiles per block
+  static constexpr int B_BYTES = SKB * NTB * 1024;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int NSTAGE = 3;
+  static constexpr int A_INST = A_BYTES / 1024, B_INST = SKB * NTB;
+  static constexpr int LOADS = (A_INST + B_INST) / 4;  // DMA instructions per wave per stage
+  static constexpr int EPI_BYTES = BM * BN * 4;
+  static constexpr int LDS = NSTAGE * STAGE > EPI_BYTES ? NSTAGE * STAGE : EPI_BYTES;
+  static_assert(A_INST % 4 == 0 && B_INST % 4 == 0, "whole DMA instructions per wave");
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+__device__ inline int swz_a(int r, int cpr) {
+  // 128-byte rows alternate bank halves: permute the 8 same-parity rows of a
+  // 16-row group; 256-byte rows all start on bank 0: spread 16 rows over 16 chunks
+  return cpr == 8 ? ((((r >> 1) & 1) << 2) | ((r >> 2) & 3)) : (r & 15);
+}
+
+__device__ inline __amdgpu_buffer_rsrc_t gemm_rsrc(const void* base, long bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p), hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  const int n = (int)(bytes > 0x7fffffffL ? 0x7fffffffL : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), (short)0,
+                                           __builtin_amdgcn_readfirstlane(n), 0x00020000);
+}
+
+// DMA stage `kb` (first k-block of the stage) into `st`; live == false (past
+// the slice) loads zeros.  Every wave issues C::LOADS instructions.
+template <class C>
+__device__ inline void tiled_issue(const GemmArgs& g, unsigned char* st, int m0, int nt0, int kb, bool live, int wave,
+                                   int lane) {
+  // A: rows m0.., k from kb*32; the record count stops at row M (zeros below)
+  const long a_rows = live ? (long)max(g.e.M - m0, 0) : 0;
+  const __amdgpu_buffer_rsrc_t ra =
+      gemm_rsrc(reinterpret_cast<const unsigned char*>(g.A) + ((size_t)m0 * g.lda + (size_t)kb * 32) * C::ESA,
+                a_rows * g.lda * C::ESA);
+  constexpr int RPI = 1024 / C::ROWB;  // A rows per DMA instruction
+#pragma unroll
+  for (int i = wave; i < C::A_INST; i += 4) {
+    const int r = i * RPI + lane / C::CPR, pc = lane % C::CPR;
+    const int c = pc ^ swz_a(r, C::CPR);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, MLA_LDS_PTR(st + i * 1024), 16,
+                                             r * g.lda * C::ESA + c * 16, 0, 0, 0);
+  }
+  // W: fragment (kb + j, nt0 + t) -> B region slot j * NTB + t
+  const long w_bytes = live ? (long)g.kblocks * g.ntiles * 1024 : 0;
+  const __amdgpu_buffer_rsrc_t rw = gemm_rsrc(g.Wp, w_bytes);
+#pragma unroll
+  for (int i = wave; i < C::B_INST; i += 4) {
+    const int j = i / C::NTB, t = i % C::NTB;
+    const int nt = nt0 + t;
+    const int off = nt < g.ntiles ? (int)((((long)(kb + j) * g.ntiles) + nt) * 1024) + lane * 16 : 0x7ffffff0;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, MLA_LDS_PTR(st + C::A_BYTES + i * 1024), 16, off, 0, 0, 0);
+  }
+}
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <typename TA, int MTW, int NTW>
+__global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmArgs g) {
+  using C = TiledCfg<TA, MTW, NTW>;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int m0 = blockIdx.y * C::BM, nt0 = blockIdx.x * C::NTB;
+  const int ks = blockIdx.z;
+  const int kb0 = ks * g.kb_per_split, kb1 = min(kb0 + g.kb_per_split, g.kblocks);
+  const int nst = (kb1 - kb0 + C::SKB - 1) / C::SKB;  // stages in this slice
+
+  f32x16 acc[MTW][NTW];
+#pragma unroll
+  for (int i = 0; i < MTW; ++i)
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) acc[i][j] = f32x16{};
+
+  // lane-constant LDS offsets
+  int a_off[MTW][2];  // [tile][chunk parity within the 16-k step]
+#pragma unroll
+  for (int i = 0; i < MTW; ++i) {
+    const int r = (wm * MTW + i) * 32 + (lane & 31);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) a_off[i][h] = r * C::ROWB;  // chunk added per k-step
+  }
+  const int a_row = lane & 31, a_hi = lane >> 5;
+  int b_off[NTW];
+#pragma unroll
+  for (int j = 0; j < NTW; ++j)
+    b_off[j] = C::A_BYTES + ((wn * NTW + j) * 2 + ((lane & 31) >> 4)) * 1024 + ((lane & 15) + 16 * a_hi) * 16;
+
+  auto compute = [&](const unsigned char* __restrict__ st, int nkb) {
+#pragma unroll
+    for (int kbl = 0; kbl < C::SKB; ++kbl) {
+      if (kbl >= nkb) break;
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {  // 16-k steps within the k-block
+        bf16x8 af[MTW], bfr[NTW];
+#pragma unroll
+        for (int i = 0; i < MTW; ++i) {
+          const int r = (wm * MTW + i) * 32 + a_row;
+          if constexpr (C::ESA == 2) {
+            const int c = (kbl * 4 + k2 * 2 + a_hi) ^ swz_a(r, C::CPR);
+            af[i] = *reinterpret_cast<const bf16x8*>(st + a_off[i][0] + c * 16);
+          } else {
+            const int c0 = (kbl * 8 + k2 * 4 + a_hi * 2) ^ swz_a(r, C::CPR);
+            const int c1 = (kbl * 8 + k2 * 4 + a_hi * 2 + 1) ^ swz_a(r, C::CPR);
+            const float4 x0 = *reinterpret_cast<const float4*>(st + a_off[i][0] + c0 * 16);
+            const float4 x1 = *reinterpret_cast<const float4*>(st + a_off[i][0] + c1 * 16);
+            af[i][0] = (__bf16)x0.x; af[i][1] = (__bf16)x0.y; af[i][2] = (__bf16)x0.z; af[i][3] = (__bf16)x0.w;
+            af[i][4] = (__bf16)x1.x; af[i][5] = (__bf16)x1.y; af[i][6] = (__bf16)x1.z; af[i][7] = (__bf16)x1.w;
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < NTW; ++j)
+          bfr[j] = *reinterpret_cast<const bf16x8*>(st + b_off[j] + kbl * C::NTB * 1024 + k2 * 32 * 16);
+#pragma unroll
+        for (int i = 0; i < MTW; ++i)
+#pragma unroll
+          for (int j = 0; j < NTW; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      }
+    }
+  };
+
+  for (int s2 = 0; s2 < C::NSTAGE - 1; ++s2)
+    tiled_issue<C>(g, smem + s2 * C::STAGE, m0, nt0, kb0 + s2 * C::SKB, s2 < nst, wave, lane);
+  for (int s2 = 0; s2 < nst; ++s2) {
+    vm_wait<(C::NSTAGE - 2) * C::LOADS>();
+    lds_barrier();
+    tiled_issue<C>(g, smem + ((s2 + C::NSTAGE - 1) % C::NSTAGE) * C::STAGE, m0, nt0,
+                   kb0 + (s2 + C::NSTAGE - 1) * C::SKB, s2 + C::NSTAGE - 1 < nst, wave, lane);
+    compute(smem + (s2 % C::NSTAGE) * C::STAGE, min(C::SKB, kb1 - kb0 - s2 * C::SKB));
+  }
+  vm_wait<0>();
+  lds_barrier();
+
+  // ---- block tile through LDS, then column-pair epilogue ----------------
+  float* tile = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int i = 0; i < MTW; ++i)
+#pragma unroll
+    for (int j = 0; j < NTW; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = (wm * MTW + i) * 32 + 8 * (r >> 2) + 4 * a_hi + (r & 3);
+        const int col = (wn * NTW + j) * 32 + (lane & 31);
+        tile[row * C::BN + col] = acc[i][j][r];
+      }
+  __syncthreads();
+  const int col0 = nt0 * 16;
+  for (int p = threadIdx.x; p < C::BM * C::BN / 2; p += 256) {
+    const int r = p / (C::BN / 2), c = (p % (C::BN / 2)) * 2;
+    const int m = m0 + r, n = col0 + c;
+    if (m >= g.e.M || n >= g.Np) continue;
+    const float v0 = tile[r * C::BN + c], v1 = tile[r * C::BN + c + 1];
+    if (g.ksplit == 1) {
+      epi_pair<__bf16>(g.e, m, n, v0, v1);
+    } else {
+      *reinterpret_cast<float2*>(g.part + ((size_t)ks * g.e.M + m) * g.Np + n) = make_float2(v0, v1);
+    }
+  }
+}
+
 // Sum of the K slices in slice order (deterministic), then the epilogue.
 template <typename T>
 __global__ __launch_bounds__(256) void splitk_epilogue_kernel(GemmArgs g) {
@@ -311,7 +495,25 @@ GemmPlan plan_gemm(int M, int K, int N, bool bf16, int n_cu) {
       }
     }
   };
-  if (mtiles <= 4) {
+  g.tiled = 0;
+  if (bf16 && M > 16 && g.kblocks % 2 == 0) {
+    // LDS-tiled kernel: 64 x 128 tiles up to 64 rows, 128 x 128 above; split
+    // K until there are two blocks per CU (slices a multiple of one stage)
+    g.tiled = 1;
+    g.MT = M > 64 ? 2 : 1;
+    g.NT = 2;
+    g.KSW = 1;
+    const int BM = 64 * g.MT, NTB = 4 * g.NT;
+    g.gx = ceil_div(g.ntiles, NTB);
+    g.gy = ceil_div(M, BM);
+    const long blocks0 = (long)g.gx * g.gy;
+    int ks = 1;
+    if (blocks0 < 2L * n_cu) ks = (int)std::min<long>((2L * n_cu + blocks0 - 1) / blocks0, std::max(1, g.kblocks / 4));
+    int kbs = ceil_div(g.kblocks, ks);
+    kbs += kbs & 1;
+    g.kb_per_split = kbs;
+    g.ksplit = ceil_div(g.kblocks, kbs);
+  } else if (mtiles <= 4) {
     // up to 64 rows: the block's waves split K; the LDS tile (4 x rows x
     // cols fp32) stays within 64 KB
     const int MT = mtiles == 1 ? 1 : (mtiles == 2 ? 2 : 4);
@@ -321,7 +523,6 @@ GemmPlan plan_gemm(int M, int K, int N, bool bf16, int n_cu) {
     consider(4, 4, 1);
   }
   g.part_bytes = g.ksplit > 1 ? (size_t)g.ksplit * (size_t)M * (size_t)g.Np * sizeof(float) : 0;
-  g.counters = 0;
   return g;
 }
 
@@ -333,6 +534,29 @@ static hipError_t launch_gemm_t(const GemmPlan& g, const GemmArgs& a, hipStream_
   const long total = (long)g.M * (g.Np / 2);
   hipLaunchKernelGGL(splitk_epilogue_kernel<T>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);
   return hipGetLastError();
+}
+
+template <typename TA, int MTW, int NTW>
+static hipError_t launch_tiled_t(const GemmPlan& g, const GemmArgs& a, hipStream_t s) {
+  using C = TiledCfg<TA, MTW, NTW>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_tiled_kernel<TA, MTW, NTW>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((gemm_tiled_kernel<TA, MTW, NTW>), dim3(g.gx, g.gy, g.ksplit), dim3(256), C::LDS, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || g.ksplit == 1) return e;
+  const long total = (long)g.M * (g.Np / 2);
+  hipLaunchKernelGGL(splitk_epilogue_kernel<__bf16>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename TA>
+static hipError_t launch_tiled_sel(const GemmPlan& g, const GemmArgs& a, hipStream_t s) {
+  return g.MT == 2 ? launch_tiled_t<TA, 2, 2>(g, a, s) : launch_tiled_t<TA, 1, 2>(g, a, s);
 }
 
 template <typename T, typename TA>
@@ -363,8 +587,7 @@ static hipError_t launch_gemm_sel(const GemmPlan& g, const GemmArgs& a, hipStrea
 }
 
 hipError_t launch_gemm(const GemmPlan& g, bool bf16, bool a_f32, const void* A, int lda, const void* Wp, float* part,
-                       int32_t* counters, const EpiArgs& e, hipStream_t s) {
-  (void)counters;
+                       const EpiArgs& e, hipStream_t s) {
   GemmArgs a{};
   a.A = A;
   a.lda = lda;
@@ -378,6 +601,7 @@ hipError_t launch_gemm(const GemmPlan& g, bool bf16, bool a_f32, const void* A, 
   a.e = e;
   a.e.M = g.M;
   a.e.N = g.N;
+  if (bf16 && g.tiled) return a_f32 ? launch_tiled_sel<float>(g, a, s) : launch_tiled_sel<__bf16>(g, a, s);
   if (bf16) {
     return a_f32 ? launch_gemm_sel<__bf16, float>(g, a, s) : launch_gemm_sel<__bf16, __bf16>(g, a, s);
   }

@@ -9,14 +9,16 @@ namespace mla {
 
 // ---------------------------------------------------------------- GEMM ----
 // y[M][N] = A[M][K] * W[K][N] with W in the packed fragment layout, followed
-// by an epilogue (store / RoPE / cache append).  One block computes a tile of
-// MT*16 rows x NGW*NT*16 columns over one K slice:
-//   KSW = 4 (decode, M <= 16): the block's 4 waves split the K slice and are
-//            summed through LDS;
-//   KSW = 1 (M > 16): the 4 waves take 4 neighbouring column groups.
+// by an epilogue (store / RoPE / cache append).  Two kernels:
+//   streaming (M <= 16, decode): one block computes MT*16 rows x NT*16
+//     columns over one K slice; its 4 waves split the slice and are summed
+//     through LDS;
+//   tiled (M > 16, bf16): a block computes BM x BN = 64*MT x 64*NT with 4
+//     waves in a 2 x 2 grid of 32x32x16 MFMA sub-tiles; A and W tiles are
+//     DMA'd into LDS through a 3-stage ring.
 // With ksplit > 1 slices, each block leaves an fp32 partial tile in the
-// workspace and the last block to finish a tile (atomic counter, reset by
-// that block) sums the slices in order and applies the epilogue.
+// workspace and a second kernel sums the slices in order and applies the
+// epilogue.
 enum EpiMode { EPI_F32 = 0, EPI_STORE_T = 1, EPI_Q = 2, EPI_APPEND = 3 };
 
 struct EpiArgs {
@@ -42,17 +44,17 @@ struct GemmPlan {
   int KB;            // k per MFMA (32 bf16, 4 fp32)
   int kblocks, ntiles;
   int MT, NT, KSW;
+  int tiled;         // 1: LDS-tiled kernel (MT, NT = 32x32 tiles per wave)
   int gx, gy;        // blocks over columns / rows
   int ksplit, kb_per_split;
   size_t part_bytes; // fp32 partial tiles (ksplit > 1)
-  int counters;      // tile counters (ksplit > 1)
 };
 
 GemmPlan plan_gemm(int M, int K, int N, bool bf16, int n_cu);
 
 // A is T (a_f32 == false) or fp32 (a_f32 == true); Wp is T.
 hipError_t launch_gemm(const GemmPlan& g, bool bf16, bool a_f32, const void* A, int lda, const void* Wp, float* part,
-                       int32_t* counters, const EpiArgs& e, hipStream_t s);
+                       const EpiArgs& e, hipStream_t s);
 
 // ------------------------------------------------------------- absorb ----
 struct AbsorbArgs {
