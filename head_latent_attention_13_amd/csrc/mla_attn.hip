@@ -224,8 +224,8 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) 
 
 // DMA one 32-row tile into an LDS stage with buffer loads whose record
 // count is the tile's visible bytes: rows at or past `vis`, a page id
-// outside the pool, and a tile past the end of the segment (`live` false)
-// all read as zeros.  Every call issues the same NINST / NW loads per wave,
+// outside the pool (which also raises error bit 2), and a tile past the end
+// of the segment (`live` false) all read as zeros.  Every call issues the same NINST / NW loads per wave,
 // so the pipeline can wait on a constant count.
 template <class C>
 __device__ inline void issue_tile(const AttnArgs& a, unsigned char* stage, int b, int k, int vis, int wave,
@@ -237,6 +237,7 @@ __device__ inline void issue_tile(const AttnArgs& a, unsigned char* stage, int b
     if (a.paged) {
       const int pg = MLA_CONST_PTR(a.page_table)[(size_t)b * a.max_pages + t0 / a.page_size];
       ok = (pg >= 0) && (pg < a.n_pages);
+      if (!ok && lane == 0) atomicOr(a.err, 2);  // flagged, then read as zeros
       gbase += ((size_t)(ok ? pg : 0) * a.page_size + (t0 % a.page_size)) * (size_t)C::ROW_BYTES;
     } else {
       gbase += ((size_t)b * a.s_max + t0) * (size_t)C::ROW_BYTES;
@@ -688,8 +689,7 @@ __device__ inline int plan_max(int v, int* wsum) {
 // used.  Outputs: srec[u] = {first tile, end tile, visible rows, 0},
 // wfl[u] = {first, last work-group} (-1 for an invalid length), wrec[w] =
 // {g0, g1, first stream, its srec}.  Invalid lengths get no tiles and raise
-// error bit 4; page ids the split kernel will follow must lie inside the
-// pool (error bit 2; the split kernel reads zeros instead).
+// error bit 4 (page ids are checked where the split kernel follows them).
 __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnArgs a, int cap) {
   constexpr int kLdsU = 2048;  // stream records staged in LDS up to this many streams
   __shared__ int wsum[kPlanThreads / 64];
@@ -703,16 +703,6 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnArgs a, int
     const int4 r = reinterpret_cast<const int4*>(a.srec)[u];
     return make_int2(r.x, r.y);
   };
-  if (a.paged) {
-    for (long i = tid; i < (long)a.B * a.max_pages; i += kPlanThreads) {
-      const int b = (int)(i / a.max_pages), p = (int)(i % a.max_pages);
-      const int L = a.kv_len[b];
-      if (L >= n_q && L <= cap && p < (L + a.page_size - 1) / a.page_size) {
-        const int pg = a.page_table[i];
-        if (pg < 0 || pg >= a.n_pages) atomicOr(a.err, 2);
-      }
-    }
-  }
   // tile prefix sums and per-stream records
   int carry = 0, nz = 0;
   for (int base = 0; base < U; base += kPlanThreads) {
