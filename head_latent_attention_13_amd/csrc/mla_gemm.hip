@@ -248,19 +248,22 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
 //
 // Block tile BM x BN = (64 MTW) x (64 NTW); 4 waves in a 2 x 2 grid, wave
 // (wm, wn) computes rows [32 MTW wm, +32 MTW) x columns [32 NTW wn, +32 NTW)
-// with v_mfma_f32_32x32x16_bf16.  A stage covers SKB = 2 k-blocks (64 k):
-//   A: BM rows x 64 k of TA, row-major, 16-byte chunk c of row r stored at
-//      chunk c ^ swz_a(r) (conflict-free 16-lane ds_read_b128 passes);
+// with v_mfma_f32_32x32x16_bf16.  A stage covers SKB k-blocks (32 k each):
+//   A: BM rows x 32 SKB k of TA, row-major, 16-byte chunk c of row r stored
+//      at chunk c ^ swz_a(r) (conflict-free 16-lane ds_read_b128 passes);
 //   W: the BN/16 packed 1 KB fragments of each k-block, in fragment order.
 // Both are DMA'd with buffer loads (rows past M and n-tiles past the weight
 // read as zeros) through a 3-stage ring, two stages in flight.
 // A 32x32x16 B operand is read straight from the packed 16-column
 // fragments: lane l takes column tile (l%32)/16, rows 8 (l/32) + 16 ks.
+// Every MFMA reads (MTW + NTW) / (MTW NTW) KB of operands from LDS, so the
+// large-M configuration uses 128 x 128 wave tiles (0.5 KB per MFMA) to stay
+// clear of the LDS bandwidth.
 // --------------------------------------------------------------------------
-template <typename TA, int MTW, int NTW>
+template <typename TA, int MTW, int NTW, int SKB_>
 struct TiledCfg {
   static constexpr int BM = 64 * MTW, BN = 64 * NTW;
-  static constexpr int SKB = 2;                      // k-blocks (32 k) per stage
+  static constexpr int SKB = SKB_;                   // k-blocks (32 k) per stage
   static constexpr int ESA = (int)sizeof(TA);
   static constexpr int ROWB = SKB * 32 * ESA;        // A bytes per row per stage
   static constexpr int CPR = ROWB / 16;              // 16-byte chunks per A row
@@ -271,16 +274,19 @@ struct TiledCfg {
   static constexpr int NSTAGE = 3;
   static constexpr int A_INST = A_BYTES / 1024, B_INST = SKB * NTB;
   static constexpr int LOADS = (A_INST + B_INST) / 4;  // DMA instructions per wave per stage
-  static constexpr int EPI_BYTES = BM * BN * 4;
-  static constexpr int LDS = NSTAGE * STAGE > EPI_BYTES ? NSTAGE * STAGE : EPI_BYTES;
+  static constexpr int EPI_BYTES = BM / 2 * BN * 4;  // the epilogue stages half the block tile at a time
+  static constexpr int ROW_META = EPI_BYTES;          // then per-row positions / cache offsets (12 B per row)
+  static constexpr int EPI_TOTAL = EPI_BYTES + BM * 12;
+  static constexpr int LDS = NSTAGE * STAGE > EPI_TOTAL ? NSTAGE * STAGE : EPI_TOTAL;
   static_assert(A_INST % 4 == 0 && B_INST % 4 == 0, "whole DMA instructions per wave");
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
 __device__ inline int swz_a(int r, int cpr) {
+  // 64-byte rows: 4 rows per 256 bytes, rows r and r+4 differ in the chunk;
   // 128-byte rows alternate bank halves: permute the 8 same-parity rows of a
   // 16-row group; 256-byte rows all start on bank 0: spread 16 rows over 16 chunks
-  return cpr == 8 ? ((((r >> 1) & 1) << 2) | ((r >> 2) & 3)) : (r & 15);
+  return cpr == 4 ? ((r >> 2) & 3) : cpr == 8 ? ((((r >> 1) & 1) << 2) | ((r >> 2) & 3)) : (r & 15);
 }
 
 __device__ inline __amdgpu_buffer_rsrc_t gemm_rsrc(const void* base, long bytes) {
@@ -323,14 +329,16 @@ __device__ inline void tiled_issue(const GemmArgs& g, unsigned char* st, int m0,
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-template <typename TA, int MTW, int NTW>
+template <typename TA, int MTW, int NTW, int SKB>
 __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmArgs g) {
-  using C = TiledCfg<TA, MTW, NTW>;
+  using C = TiledCfg<TA, MTW, NTW, SKB>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave & 1, wn = wave >> 1;
-  const int m0 = blockIdx.y * C::BM, nt0 = blockIdx.x * C::NTB;
+  // row blocks vary fastest: blocks running together share their weight
+  // columns (each W tile is fetched once) while A, M rows deep, stays cached
+  const int m0 = blockIdx.x * C::BM, nt0 = blockIdx.y * C::NTB;
   const int ks = blockIdx.z;
   const int kb0 = ks * g.kb_per_split, kb1 = min(kb0 + g.kb_per_split, g.kblocks);
   const int nst = (kb1 - kb0 + C::SKB - 1) / C::SKB;  // stages in this slice
@@ -355,37 +363,57 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmArgs g) {
   for (int j = 0; j < NTW; ++j)
     b_off[j] = C::A_BYTES + ((wn * NTW + j) * 2 + ((lane & 31) >> 4)) * 1024 + ((lane & 15) + 16 * a_hi) * 16;
 
-  auto compute = [&](const unsigned char* __restrict__ st, int nkb) {
+  // Fragments of 16-k step q of a stage (q = 2 kbl + k2).
+  auto load_a = [&](const unsigned char* __restrict__ st, int q, bf16x8 (&af)[MTW]) {
+    const int kbl = q >> 1, k2 = q & 1;
 #pragma unroll
-    for (int kbl = 0; kbl < C::SKB; ++kbl) {
-      if (kbl >= nkb) break;
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {  // 16-k steps within the k-block
-        bf16x8 af[MTW], bfr[NTW];
-#pragma unroll
-        for (int i = 0; i < MTW; ++i) {
-          const int r = (wm * MTW + i) * 32 + a_row;
-          if constexpr (C::ESA == 2) {
-            const int c = (kbl * 4 + k2 * 2 + a_hi) ^ swz_a(r, C::CPR);
-            af[i] = *reinterpret_cast<const bf16x8*>(st + a_off[i][0] + c * 16);
-          } else {
-            const int c0 = (kbl * 8 + k2 * 4 + a_hi * 2) ^ swz_a(r, C::CPR);
-            const int c1 = (kbl * 8 + k2 * 4 + a_hi * 2 + 1) ^ swz_a(r, C::CPR);
-            const float4 x0 = *reinterpret_cast<const float4*>(st + a_off[i][0] + c0 * 16);
-            const float4 x1 = *reinterpret_cast<const float4*>(st + a_off[i][0] + c1 * 16);
-            af[i][0] = (__bf16)x0.x; af[i][1] = (__bf16)x0.y; af[i][2] = (__bf16)x0.z; af[i][3] = (__bf16)x0.w;
-            af[i][4] = (__bf16)x1.x; af[i][5] = (__bf16)x1.y; af[i][6] = (__bf16)x1.z; af[i][7] = (__bf16)x1.w;
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < NTW; ++j)
-          bfr[j] = *reinterpret_cast<const bf16x8*>(st + b_off[j] + kbl * C::NTB * 1024 + k2 * 32 * 16);
-#pragma unroll
-        for (int i = 0; i < MTW; ++i)
-#pragma unroll
-          for (int j = 0; j < NTW; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    for (int i = 0; i < MTW; ++i) {
+      const int r = (wm * MTW + i) * 32 + a_row;
+      if constexpr (C::ESA == 2) {
+        const int c = (kbl * 4 + k2 * 2 + a_hi) ^ swz_a(r, C::CPR);
+        af[i] = *reinterpret_cast<const bf16x8*>(st + a_off[i][0] + c * 16);
+      } else {
+        const int c0 = (kbl * 8 + k2 * 4 + a_hi * 2) ^ swz_a(r, C::CPR);
+        const int c1 = (kbl * 8 + k2 * 4 + a_hi * 2 + 1) ^ swz_a(r, C::CPR);
+        const float4 x0 = *reinterpret_cast<const float4*>(st + a_off[i][0] + c0 * 16);
+        const float4 x1 = *reinterpret_cast<const float4*>(st + a_off[i][0] + c1 * 16);
+        af[i][0] = (__bf16)x0.x; af[i][1] = (__bf16)x0.y; af[i][2] = (__bf16)x0.z; af[i][3] = (__bf16)x0.w;
+        af[i][4] = (__bf16)x1.x; af[i][5] = (__bf16)x1.y; af[i][6] = (__bf16)x1.z; af[i][7] = (__bf16)x1.w;
       }
     }
+  };
+  auto load_b = [&](const unsigned char* __restrict__ st, int q, bf16x8 (&bf)[NTW]) {
+    const int kbl = q >> 1, k2 = q & 1;
+#pragma unroll
+    for (int j = 0; j < NTW; ++j)
+      bf[j] = *reinterpret_cast<const bf16x8*>(st + b_off[j] + kbl * C::NTB * 1024 + k2 * 32 * 16);
+  };
+  // One stage: the fragments of all its 16-k steps are read first, then
+  // the MFMAs run (one LDS round trip per stage instead of one per step;
+  // the scheduling barriers keep the compiler from re-serialising the reads
+  // behind the MFMAs that use them).
+  auto compute = [&](const unsigned char* __restrict__ st, int nkb) {
+    constexpr int NQ = 2 * C::SKB;
+    const int nq = 2 * min(nkb, C::SKB);
+    bf16x8 af[NQ][MTW], bf[NQ][NTW];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      if (q < nq) {
+        load_a(st, q, af[q]);
+        load_b(st, q, bf[q]);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      if (q >= nq) break;
+#pragma unroll
+      for (int i = 0; i < MTW; ++i)
+#pragma unroll
+        for (int j = 0; j < NTW; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[q][i], bf[q][j], acc[i][j], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, NQ * (MTW + NTW) * (C::ESA == 2 ? 1 : 1), 0);  // DS reads
+    __builtin_amdgcn_sched_group_barrier(0x008, NQ * MTW * NTW, 0);                          // MFMAs
   };
 
   for (int s2 = 0; s2 < C::NSTAGE - 1; ++s2)
@@ -400,30 +428,128 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmArgs g) {
   vm_wait<0>();
   lds_barrier();
 
-  // ---- block tile through LDS, then column-pair epilogue ----------------
+  // ---- epilogue -----------------------------------------------------------
+  // Per-row values are looked up once per block and kept in LDS (a load per
+  // element pair would expose a memory round trip in every iteration): the
+  // token position (RoPE, cache slot) and, when appending, the element
+  // offset of the destination cache row (-1: no valid slot).  The block tile
+  // then goes through LDS one half of its rows at a time; each thread owns
+  // one column pair, so its RoPE frequency is set up once.
   float* tile = reinterpret_cast<float*>(smem);
-#pragma unroll
-  for (int i = 0; i < MTW; ++i)
-#pragma unroll
-    for (int j = 0; j < NTW; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = (wm * MTW + i) * 32 + 8 * (r >> 2) + 4 * a_hi + (r & 3);
-        const int col = (wn * NTW + j) * 32 + (lane & 31);
-        tile[row * C::BN + col] = acc[i][j][r];
+  int* row_pos = reinterpret_cast<int*>(smem + C::ROW_META);
+  long long* row_dst = reinterpret_cast<long long*>(smem + C::ROW_META + C::BM * 4);
+  const EpiArgs& e = g.e;
+  const bool rope_mode = g.ksplit == 1 && (e.mode == EPI_Q || e.mode == EPI_APPEND);
+  if (rope_mode) {
+    for (int r = threadIdx.x; r < C::BM; r += 256) {
+      const int m = m0 + r;
+      int pos = 0;
+      long long dst = -1;
+      if (m < e.M) {
+        const int b = m / e.n_q, t = m - b * e.n_q;
+        pos = (e.mode == EPI_Q) ? e.kv_len[b] - e.n_q + t : e.pos[b] + t;
+        if (e.mode == EPI_APPEND) {
+          if (e.paged) {
+            if (pos < 0 || pos >= e.max_pages * e.page_size) {
+              atomicOr(e.err, 1);
+            } else {
+              const int pg = e.page_table[(size_t)b * e.max_pages + pos / e.page_size];
+              if (pg < 0 || pg >= e.n_pages)
+                atomicOr(e.err, 2);
+              else
+                dst = ((long long)pg * e.page_size + pos % e.page_size) * e.row;
+            }
+          } else if (pos < 0 || pos >= e.s_max) {
+            atomicOr(e.err, 1);
+          } else {
+            dst = ((long long)b * e.s_max + pos) * e.row;
+          }
+        }
       }
-  __syncthreads();
-  const int col0 = nt0 * 16;
-  for (int p = threadIdx.x; p < C::BM * C::BN / 2; p += 256) {
-    const int r = p / (C::BN / 2), c = (p % (C::BN / 2)) * 2;
-    const int m = m0 + r, n = col0 + c;
-    if (m >= g.e.M || n >= g.Np) continue;
-    const float v0 = tile[r * C::BN + c], v1 = tile[r * C::BN + c + 1];
-    if (g.ksplit == 1) {
-      epi_pair<__bf16>(g.e, m, n, v0, v1);
-    } else {
-      *reinterpret_cast<float2*>(g.part + ((size_t)ks * g.e.M + m) * g.Np + n) = make_float2(v0, v1);
+      row_pos[r] = pos;
+      row_dst[r] = dst;
     }
+  }
+  const int col0 = nt0 * 16;
+  constexpr int HM = C::BM / 2;       // rows per half: the rows of the waves with wm == half
+  constexpr int CPB = C::BN / 2;      // column pairs per block row
+  constexpr int RSTEP = 256 / CPB;    // rows advanced per thread iteration
+  const int cp = threadIdx.x % CPB, r_first = threadIdx.x / CPB;
+  const int n = col0 + 2 * cp;
+  // column role: latent / rope pair j (rotation frequency in revolutions per position)
+  bool rope_col = false;
+  double rev_per_pos = 0.0;
+  if (rope_mode && n < e.N) {
+    const int f = n % e.row;
+    if (f >= e.d_latent) {
+      const int j = (f - e.d_latent) >> 1;
+      rope_col = true;
+      rev_per_pos = exp2(-(2.0 * (double)j / (double)e.d_rope) * log2((double)e.rope_base)) * 0.15915494309189535;
+    }
+  }
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    if (wm == half) {
+#pragma unroll
+      for (int i = 0; i < MTW; ++i)
+#pragma unroll
+        for (int j = 0; j < NTW; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = i * 32 + 8 * (r >> 2) + 4 * a_hi + (r & 3);
+            const int col = (wn * NTW + j) * 32 + (lane & 31);
+            tile[row * C::BN + col] = acc[i][j][r];
+          }
+    }
+    __syncthreads();
+    if (n < g.Np) {
+      for (int r = r_first; r < HM; r += RSTEP) {
+        const int rb = half * HM + r;  // row within the block
+        const int m = m0 + rb;
+        if (m >= e.M) break;
+        float v0 = tile[r * C::BN + 2 * cp], v1 = tile[r * C::BN + 2 * cp + 1];
+        if (g.ksplit > 1) {
+          *reinterpret_cast<float2*>(g.part + ((size_t)ks * e.M + m) * g.Np + n) = make_float2(v0, v1);
+          continue;
+        }
+        if (n >= e.N) continue;
+        const bool has1 = n + 1 < e.N;
+        if (e.mode == EPI_F32) {
+          float* y = reinterpret_cast<float*>(e.out) + (size_t)m * e.N + n;
+          if (has1)
+            *reinterpret_cast<float2*>(y) = make_float2(v0, v1);
+          else
+            y[0] = v0;
+          continue;
+        }
+        if (rope_col) {
+          // angle reduced to (-1/2, 1/2] revolutions in fp64, then the
+          // hardware sine / cosine (argument in revolutions)
+          double rev = (double)row_pos[rb] * rev_per_pos;
+          rev -= rint(rev);
+          const float rf = (float)rev;
+          const float c = __builtin_amdgcn_cosf(rf), sn = __builtin_amdgcn_sinf(rf);
+          const float a0 = v0, a1 = v1;
+          v0 = a0 * c - a1 * sn;
+          v1 = a0 * sn + a1 * c;
+        }
+        __bf16* y;
+        if (e.mode == EPI_APPEND) {
+          const long long d = row_dst[rb];
+          if (d < 0) continue;
+          y = reinterpret_cast<__bf16*>(e.pool) + d + n;
+        } else {
+          y = reinterpret_cast<__bf16*>(e.out) + (size_t)m * e.N + n;
+        }
+        if (has1) {
+          __bf16 pr[2] = {(__bf16)v0, (__bf16)v1};
+          *reinterpret_cast<uint32_t*>(y) = *reinterpret_cast<const uint32_t*>(pr);
+        } else {
+          y[0] = (__bf16)v0;
+        }
+      }
+    }
+    __syncthreads();
   }
 }
 
@@ -496,21 +622,26 @@ GemmPlan plan_gemm(int M, int K, int N, bool bf16, int n_cu) {
     }
   };
   g.tiled = 0;
-  if (bf16 && M > 16 && g.kblocks % 2 == 0) {
-    // LDS-tiled kernel: 64 x 128 tiles up to 64 rows, 128 x 128 above; split
-    // K until there are two blocks per CU (slices a multiple of one stage)
+  const bool big = M >= 256 && g.ntiles >= 64;  // 256 x 256 tiles, one k-block per stage
+  if (bf16 && M > 16 && (big || g.kblocks % 2 == 0)) {
+    // LDS-tiled kernel: 64 x 128 tiles up to 64 rows, 128 x 128 up to 255,
+    // 256 x 256 above; split K until there are two blocks per CU (slices a
+    // multiple of one stage), except that 256 x 256 tiles (one block per
+    // CU) only split when there are fewer blocks than about 0.8 CUs
     g.tiled = 1;
-    g.MT = M > 64 ? 2 : 1;
-    g.NT = 2;
+    g.MT = big ? 4 : (M > 64 ? 2 : 1);
+    g.NT = big ? 4 : 2;
     g.KSW = 1;
+    const int skb = big ? 1 : 2;
     const int BM = 64 * g.MT, NTB = 4 * g.NT;
     g.gx = ceil_div(g.ntiles, NTB);
     g.gy = ceil_div(M, BM);
     const long blocks0 = (long)g.gx * g.gy;
+    const long want = big ? (long)(0.8 * n_cu) : 2L * n_cu;
     int ks = 1;
-    if (blocks0 < 2L * n_cu) ks = (int)std::min<long>((2L * n_cu + blocks0 - 1) / blocks0, std::max(1, g.kblocks / 4));
+    if (blocks0 < want) ks = (int)std::min<long>((want + blocks0 - 1) / blocks0, std::max(1, g.kblocks / 4));
     int kbs = ceil_div(g.kblocks, ks);
-    kbs += kbs & 1;
+    kbs = ceil_div(kbs, skb) * skb;
     g.kb_per_split = kbs;
     g.ksplit = ceil_div(g.kblocks, kbs);
   } else if (mtiles <= 4) {
@@ -536,17 +667,17 @@ static hipError_t launch_gemm_t(const GemmPlan& g, const GemmArgs& a, hipStream_
   return hipGetLastError();
 }
 
-template <typename TA, int MTW, int NTW>
+template <typename TA, int MTW, int NTW, int SKB>
 static hipError_t launch_tiled_t(const GemmPlan& g, const GemmArgs& a, hipStream_t s) {
-  using C = TiledCfg<TA, MTW, NTW>;
+  using C = TiledCfg<TA, MTW, NTW, SKB>;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_tiled_kernel<TA, MTW, NTW>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_tiled_kernel<TA, MTW, NTW, SKB>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((gemm_tiled_kernel<TA, MTW, NTW>), dim3(g.gx, g.gy, g.ksplit), dim3(256), C::LDS, s, a);
+  hipLaunchKernelGGL((gemm_tiled_kernel<TA, MTW, NTW, SKB>), dim3(g.gy, g.gx, g.ksplit), dim3(256), C::LDS, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || g.ksplit == 1) return e;
   const long total = (long)g.M * (g.Np / 2);
@@ -556,7 +687,8 @@ static hipError_t launch_tiled_t(const GemmPlan& g, const GemmArgs& a, hipStream
 
 template <typename TA>
 static hipError_t launch_tiled_sel(const GemmPlan& g, const GemmArgs& a, hipStream_t s) {
-  return g.MT == 2 ? launch_tiled_t<TA, 2, 2>(g, a, s) : launch_tiled_t<TA, 1, 2>(g, a, s);
+  if (g.MT == 4) return launch_tiled_t<TA, 4, 4, 1>(g, a, s);
+  return g.MT == 2 ? launch_tiled_t<TA, 2, 2, 2>(g, a, s) : launch_tiled_t<TA, 1, 2, 2>(g, a, s);
 }
 
 template <typename T, typename TA>
