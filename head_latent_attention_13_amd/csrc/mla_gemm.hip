@@ -297,34 +297,55 @@ __device__ inline __amdgpu_buffer_rsrc_t gemm_rsrc(const void* base, long bytes)
                                            __builtin_amdgcn_readfirstlane(n), 0x00020000);
 }
 
-// DMA stage `kb` (first k-block of the stage) into `st`; live == false (past
-// the slice) loads zeros.  Every wave issues C::LOADS instructions.
+// DMA of stage `kb` (first k-block of the stage) into `st`; live == false
+// (past the slice) loads zeros.  Every wave issues C::LOADS instructions;
+// instruction u of a wave is one of its A rows-group loads (u < A_INST/4) or
+// one of its packed W fragments.
+template <class C>
+struct TiledDma {
+  unsigned char* st;
+  int m0, nt0, kb;
+  bool live;
+};
+template <class C>
+__device__ inline TiledDma<C> tiled_dma(const GemmArgs&, unsigned char* st, int m0, int nt0, int kb, bool live) {
+  return TiledDma<C>{st, m0, nt0, kb, live};
+}
+// (Not a template: the tile constants come in as arguments and fold at the
+// inlined call sites.)
+__device__ inline void tiled_dma_load(const GemmArgs& g, unsigned char* st, int m0, int nt0, int kb, bool live, int u,
+                                      int wave, int lane, int a_inst, int rowb, int esa, int ntb, int a_bytes) {
+  const int aw = a_inst / 4, cpr = rowb / 16;
+  if (u < aw) {
+    // A: rows m0.., k from kb*32; the record count stops at row M (zeros below)
+    const long a_rows = live ? (long)max(g.e.M - m0, 0) : 0;
+    const __amdgpu_buffer_rsrc_t ra =
+        gemm_rsrc(reinterpret_cast<const unsigned char*>(g.A) + ((size_t)m0 * g.lda + (size_t)kb * 32) * esa,
+                  a_rows * g.lda * esa);
+    const int i = wave + 4 * u;
+    const int r = i * (1024 / rowb) + lane / cpr, pc = lane % cpr;
+    const int c = pc ^ swz_a(r, cpr);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, MLA_LDS_PTR(st + i * 1024), 16, r * g.lda * esa + c * 16, 0, 0, 0);
+  } else {
+    // W: fragment (kb + j, nt0 + t) -> B region slot j * NTB + t
+    const __amdgpu_buffer_rsrc_t rw = gemm_rsrc(g.Wp, live ? (long)g.kblocks * g.ntiles * 1024 : 0);
+    const int i = wave + 4 * (u - aw);
+    const int j = i / ntb, t = i % ntb;
+    const int nt = nt0 + t;
+    const int off = nt < g.ntiles ? (int)((((long)(kb + j) * g.ntiles) + nt) * 1024) + lane * 16 : 0x7ffffff0;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, MLA_LDS_PTR(st + a_bytes + i * 1024), 16, off, 0, 0, 0);
+  }
+}
+template <class C>
+__device__ inline void tiled_dma_one(const GemmArgs& g, const TiledDma<C>& d, int u, int wave, int lane) {
+  tiled_dma_load(g, d.st, d.m0, d.nt0, d.kb, d.live, u, wave, lane, C::A_INST, C::ROWB, C::ESA, C::NTB, C::A_BYTES);
+}
 template <class C>
 __device__ inline void tiled_issue(const GemmArgs& g, unsigned char* st, int m0, int nt0, int kb, bool live, int wave,
                                    int lane) {
-  // A: rows m0.., k from kb*32; the record count stops at row M (zeros below)
-  const long a_rows = live ? (long)max(g.e.M - m0, 0) : 0;
-  const __amdgpu_buffer_rsrc_t ra =
-      gemm_rsrc(reinterpret_cast<const unsigned char*>(g.A) + ((size_t)m0 * g.lda + (size_t)kb * 32) * C::ESA,
-                a_rows * g.lda * C::ESA);
-  constexpr int RPI = 1024 / C::ROWB;  // A rows per DMA instruction
+  const TiledDma<C> d = tiled_dma<C>(g, st, m0, nt0, kb, live);
 #pragma unroll
-  for (int i = wave; i < C::A_INST; i += 4) {
-    const int r = i * RPI + lane / C::CPR, pc = lane % C::CPR;
-    const int c = pc ^ swz_a(r, C::CPR);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, MLA_LDS_PTR(st + i * 1024), 16,
-                                             r * g.lda * C::ESA + c * 16, 0, 0, 0);
-  }
-  // W: fragment (kb + j, nt0 + t) -> B region slot j * NTB + t
-  const long w_bytes = live ? (long)g.kblocks * g.ntiles * 1024 : 0;
-  const __amdgpu_buffer_rsrc_t rw = gemm_rsrc(g.Wp, w_bytes);
-#pragma unroll
-  for (int i = wave; i < C::B_INST; i += 4) {
-    const int j = i / C::NTB, t = i % C::NTB;
-    const int nt = nt0 + t;
-    const int off = nt < g.ntiles ? (int)((((long)(kb + j) * g.ntiles) + nt) * 1024) + lane * 16 : 0x7ffffff0;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, MLA_LDS_PTR(st + C::A_BYTES + i * 1024), 16, off, 0, 0, 0);
-  }
+  for (int u = 0; u < C::LOADS; ++u) tiled_dma_one<C>(g, d, u, wave, lane);
 }
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -392,8 +413,11 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmArgs g) {
   // the MFMAs run (one LDS round trip per stage instead of one per step;
   // the scheduling barriers keep the compiler from re-serialising the reads
   // behind the MFMAs that use them).
-  auto compute = [&](const unsigned char* __restrict__ st, int nkb) {
+  // (The DMA of a later stage is issued between the MFMAs: issued back to
+  // back the loads would stall the wave on the address unit's queue.)
+  auto compute = [&](const unsigned char* __restrict__ st, int nkb, const TiledDma<C>& dma) {
     constexpr int NQ = 2 * C::SKB;
+    constexpr int NMF = NQ * MTW * NTW;
     const int nq = 2 * min(nkb, C::SKB);
     bf16x8 af[NQ][MTW], bf[NQ][NTW];
 #pragma unroll
@@ -403,17 +427,22 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmArgs g) {
         load_b(st, q, bf[q]);
       }
     }
+    int mf = 0, issued = 0;
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
-      if (q >= nq) break;
 #pragma unroll
       for (int i = 0; i < MTW; ++i)
 #pragma unroll
-        for (int j = 0; j < NTW; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[q][i], bf[q][j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < NTW; ++j) {
+          if (q < nq) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[q][i], bf[q][j], acc[i][j], 0, 0, 0);
+          ++mf;
+          // DMA instruction u goes after MFMA (u + 1) * NMF / LOADS
+          while (issued < C::LOADS && mf * C::LOADS >= (issued + 1) * NMF) {
+            tiled_dma_one<C>(g, dma, issued, wave, lane);
+            ++issued;
+          }
+        }
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, NQ * (MTW + NTW) * (C::ESA == 2 ? 1 : 1), 0);  // DS reads
-    __builtin_amdgcn_sched_group_barrier(0x008, NQ * MTW * NTW, 0);                          // MFMAs
   };
 
   for (int s2 = 0; s2 < C::NSTAGE - 1; ++s2)
@@ -421,9 +450,9 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmArgs g) {
   for (int s2 = 0; s2 < nst; ++s2) {
     vm_wait<(C::NSTAGE - 2) * C::LOADS>();
     lds_barrier();
-    tiled_issue<C>(g, smem + ((s2 + C::NSTAGE - 1) % C::NSTAGE) * C::STAGE, m0, nt0,
-                   kb0 + (s2 + C::NSTAGE - 1) * C::SKB, s2 + C::NSTAGE - 1 < nst, wave, lane);
-    compute(smem + (s2 % C::NSTAGE) * C::STAGE, min(C::SKB, kb1 - kb0 - s2 * C::SKB));
+    const TiledDma<C> dma = tiled_dma<C>(g, smem + ((s2 + C::NSTAGE - 1) % C::NSTAGE) * C::STAGE, m0, nt0,
+                                         kb0 + (s2 + C::NSTAGE - 1) * C::SKB, s2 + C::NSTAGE - 1 < nst);
+    compute(smem + (s2 % C::NSTAGE) * C::STAGE, min(C::SKB, kb1 - kb0 - s2 * C::SKB), dma);
   }
   vm_wait<0>();
   lds_barrier();
@@ -502,50 +531,79 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmArgs g) {
           }
     }
     __syncthreads();
-    if (n < g.Np) {
-      for (int r = r_first; r < HM; r += RSTEP) {
-        const int rb = half * HM + r;  // row within the block
-        const int m = m0 + rb;
-        if (m >= e.M) break;
-        float v0 = tile[r * C::BN + 2 * cp], v1 = tile[r * C::BN + 2 * cp + 1];
-        if (g.ksplit > 1) {
-          *reinterpret_cast<float2*>(g.part + ((size_t)ks * e.M + m) * g.Np + n) = make_float2(v0, v1);
-          continue;
+    // rows r_first + RSTEP u: UR rows per batch, their LDS reads issued
+    // together; the mode is uniform, so each mode has its own loop
+    constexpr int UR = 8;
+    const int mlim = e.M - (m0 + half * HM);  // rows of this half that exist
+    auto rows = [&](auto body) {
+      for (int r0 = r_first; r0 < HM; r0 += UR * RSTEP) {
+        float2 v[UR];
+#pragma unroll
+        for (int u = 0; u < UR; ++u) {
+          const int r = r0 + u * RSTEP;
+          v[u] = r < HM ? *reinterpret_cast<const float2*>(tile + r * C::BN + 2 * cp) : make_float2(0.f, 0.f);
         }
-        if (n >= e.N) continue;
+#pragma unroll
+        for (int u = 0; u < UR; ++u) {
+          const int r = r0 + u * RSTEP;
+          if (r < HM && r < mlim) body(r, v[u]);
+        }
+      }
+    };
+    if (n < g.Np) {
+      if (g.ksplit > 1) {
+        rows([&](int r, float2 v) {
+          *reinterpret_cast<float2*>(g.part + ((size_t)ks * e.M + m0 + half * HM + r) * g.Np + n) = v;
+        });
+      } else if (n < e.N) {
         const bool has1 = n + 1 < e.N;
         if (e.mode == EPI_F32) {
-          float* y = reinterpret_cast<float*>(e.out) + (size_t)m * e.N + n;
-          if (has1)
-            *reinterpret_cast<float2*>(y) = make_float2(v0, v1);
-          else
-            y[0] = v0;
-          continue;
-        }
-        if (rope_col) {
-          // angle reduced to (-1/2, 1/2] revolutions in fp64, then the
-          // hardware sine / cosine (argument in revolutions)
-          double rev = (double)row_pos[rb] * rev_per_pos;
-          rev -= rint(rev);
-          const float rf = (float)rev;
-          const float c = __builtin_amdgcn_cosf(rf), sn = __builtin_amdgcn_sinf(rf);
-          const float a0 = v0, a1 = v1;
-          v0 = a0 * c - a1 * sn;
-          v1 = a0 * sn + a1 * c;
-        }
-        __bf16* y;
-        if (e.mode == EPI_APPEND) {
-          const long long d = row_dst[rb];
-          if (d < 0) continue;
-          y = reinterpret_cast<__bf16*>(e.pool) + d + n;
+          rows([&](int r, float2 v) {
+            float* y = reinterpret_cast<float*>(e.out) + (size_t)(m0 + half * HM + r) * e.N + n;
+            if (has1)
+              *reinterpret_cast<float2*>(y) = v;
+            else
+              y[0] = v.x;
+          });
         } else {
-          y = reinterpret_cast<__bf16*>(e.out) + (size_t)m * e.N + n;
-        }
-        if (has1) {
-          __bf16 pr[2] = {(__bf16)v0, (__bf16)v1};
-          *reinterpret_cast<uint32_t*>(y) = *reinterpret_cast<const uint32_t*>(pr);
-        } else {
-          y[0] = (__bf16)v0;
+          // bf16 pair store; RoPE rotation for rope columns (angle reduced to
+          // (-1/2, 1/2] revolutions in fp64, then the hardware sine / cosine,
+          // whose argument is in revolutions)
+          auto store = [&](__bf16* y, float v0, float v1) {
+            if (has1) {
+              __bf16 pr[2] = {(__bf16)v0, (__bf16)v1};
+              *reinterpret_cast<uint32_t*>(y) = *reinterpret_cast<const uint32_t*>(pr);
+            } else {
+              y[0] = (__bf16)v0;
+            }
+          };
+          auto rotate = [&](int rb, float2& v) {
+            double rev = (double)row_pos[rb] * rev_per_pos;
+            rev -= rint(rev);
+            const float rf = (float)rev;
+            const float c = __builtin_amdgcn_cosf(rf), sn = __builtin_amdgcn_sinf(rf);
+            const float a0 = v.x, a1 = v.y;
+            v.x = a0 * c - a1 * sn;
+            v.y = a0 * sn + a1 * c;
+          };
+          if (e.mode == EPI_APPEND) {
+            rows([&](int r, float2 v) {
+              const int rb = half * HM + r;
+              const long long d = row_dst[rb];
+              if (rope_col) rotate(rb, v);
+              if (d >= 0) store(reinterpret_cast<__bf16*>(e.pool) + d + n, v.x, v.y);
+            });
+          } else if (rope_col) {
+            rows([&](int r, float2 v) {
+              const int rb = half * HM + r;
+              rotate(rb, v);
+              store(reinterpret_cast<__bf16*>(e.out) + (size_t)(m0 + rb) * e.N + n, v.x, v.y);
+            });
+          } else {
+            rows([&](int r, float2 v) {
+              store(reinterpret_cast<__bf16*>(e.out) + (size_t)(m0 + half * HM + r) * e.N + n, v.x, v.y);
+            });
+          }
         }
       }
     }
