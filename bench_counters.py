@@ -27,9 +27,6 @@ import sys
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CALLS = ("mla_compress_append", "mla_q_proj", "mla_attention", "mla_out_proj")
-# kernels each call launches, in order (split-K GEMMs add an epilogue kernel)
-CALL_OF_POSITION = ("mla_compress_append", "mla_compress_append", "mla_q_proj", "mla_q_proj", "mla_q_proj",
-                    "mla_attention", "mla_attention", "mla_attention", "mla_out_proj", "mla_out_proj")
 COPY_MB = 512
 
 
@@ -74,12 +71,35 @@ def counter_per_dispatch(path):
 
 
 def last_step(per_dispatch):
-    """The 10 dispatches of the last bench step, mapped to their call."""
+    """The dispatches of the last bench step, each mapped to its call.
+
+    A step is: the append GEMM, the two q-projection GEMMs, the attention
+    plan / split / merge kernels, the output GEMM; a GEMM whose K range is
+    split is followed by its epilogue kernel.  The step is anchored at its
+    attention plan kernel."""
     ids = [d for d in sorted(per_dispatch) if mla_kernel(per_dispatch[d][0])]
-    # the breakdown pass ends the run; the absorb kernels come first, so the
-    # last 10 mla dispatches are one whole step
-    step = ids[-len(CALL_OF_POSITION):]
-    return [(CALL_OF_POSITION[i], per_dispatch[d][0], per_dispatch[d][1]) for i, d in enumerate(step)]
+    names = [per_dispatch[d][0] for d in ids]
+    plan = max(i for i, n in enumerate(names) if "attn_plan" in n)
+
+    def gemm_groups_before(end, count):
+        groups, i = [], end - 1
+        while len(groups) < count:
+            g = [i]
+            if "splitk_epilogue" in names[i]:
+                i -= 1
+                g.insert(0, i)
+            groups.insert(0, g)
+            i -= 1
+        return groups
+
+    pre = gemm_groups_before(plan, 3)
+    calls = [("mla_compress_append", i) for i in pre[0]] + [("mla_q_proj", i) for g in pre[1:] for i in g]
+    calls += [("mla_attention", plan), ("mla_attention", plan + 1), ("mla_attention", plan + 2)]
+    i = plan + 3
+    calls.append(("mla_out_proj", i))
+    if i + 1 < len(names) and "splitk_epilogue" in names[i + 1]:
+        calls.append(("mla_out_proj", i + 1))
+    return [(c, names[i], per_dispatch[ids[i]][1]) for c, i in calls]
 
 
 def main():
@@ -87,23 +107,31 @@ def main():
     ap.add_argument("--config", type=int, default=1)
     ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "counters"))
     ap.add_argument("--profiles-dir", default=os.path.join(ROOT, "profiles"))
+    ap.add_argument("--summarize-only", action="store_true",
+                    help="rebuild the summaries from the profiler output already under --out")
     args = ap.parse_args()
+    # the profiler runs from /tmp: every path handed to it is absolute
+    args.out = os.path.abspath(args.out)
+    args.profiles_dir = os.path.abspath(args.profiles_dir)
     os.makedirs(args.out, exist_ok=True)
     py = sys.executable
     bench = [py, os.path.join(ROOT, "bench.py"), "--config", str(args.config), "--no-cpu-baseline"]
     stats_cmd = ["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d",
                  os.path.join(args.out, "trace"), "-o", "run", "--"] + bench + ["--steps", "20", "--warmup", "5"]
-    run(stats_cmd, args.out, "trace", 600)
+    if not args.summarize_only:
+        run(stats_cmd, args.out, "trace", 600)
     pmc = {}
     for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
         cmd = ["timeout", "-s", "KILL", "120", "rocprofv3", "--pmc", ctr, "--output-format", "csv", "-d",
                os.path.join(args.out, "pmc_" + ctr), "-o", "run", "--"] + bench + ["--steps", "3", "--warmup", "1"]
-        run(cmd, args.out, "pmc_" + ctr, 180)
+        if not args.summarize_only:
+            run(cmd, args.out, "pmc_" + ctr, 180)
         pmc[ctr] = counter_per_dispatch(find(args.out, "pmc_" + ctr, "counter_collection.csv"))
         cmd = ["timeout", "-s", "KILL", "60", "rocprofv3", "--pmc", ctr, "--output-format", "csv", "-d",
                os.path.join(args.out, "copy_" + ctr), "-o", "run", "--", py, os.path.join(ROOT, "bench.py"),
                "--copy-calib-mb", str(COPY_MB), "--steps", "3"]
-        run(cmd, args.out, "copy_" + ctr, 120)
+        if not args.summarize_only:
+            run(cmd, args.out, "copy_" + ctr, 120)
         pmc["copy_" + ctr] = counter_per_dispatch(find(args.out, "copy_" + ctr, "counter_collection.csv"))
 
     # calibration: the copy reads and writes COPY_MB MiB per launch
