@@ -107,10 +107,10 @@ WsLayout ws_layout(const mla_dims* d, int batch, int n_q) {
   const bool bf = is_bf16(d);
   const int M = batch * n_q, R = row_width(d), H = d->n_heads;
   const int ncu = device_cus();
-  W.g_app = plan_gemm(M, d->d_model, R, bf, ncu);
-  W.g_cq = plan_gemm(M, d->d_model, d->d_q_latent, bf, ncu);
-  W.g_q = plan_gemm(M, d->d_q_latent, H * R, bf, ncu);
-  W.g_out = plan_gemm(M, H * d->d_latent, d->d_model, bf, ncu);
+  W.g_app = plan_gemm(M, d->d_model, R, bf, false, ncu);
+  W.g_cq = plan_gemm(M, d->d_model, d->d_q_latent, bf, false, ncu);
+  W.g_q = plan_gemm(M, d->d_q_latent, H * R, bf, false, ncu);
+  W.g_out = plan_gemm(M, H * d->d_latent, d->d_model, bf, true, ncu);
   W.G = ncu;
   W.V = M;
   size_t o = 0;
@@ -192,6 +192,9 @@ mla_status attention_impl(const mla_dims* d, const WsLayout& W, const void* q, c
   a.page_table = c->page_table;
   a.paged = c->page_table != nullptr;
   a.page_size = a.paged ? c->page_size : 32;
+  a.tpp_shift = -1;
+  for (int sh = 0; sh < 31; ++sh)
+    if ((32 << sh) == a.page_size) a.tpp_shift = sh;
   a.n_pages = c->n_pages;
   a.max_pages = c->max_pages_per_seq;
   a.s_max = c->s_max;

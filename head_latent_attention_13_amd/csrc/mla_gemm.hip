@@ -260,7 +260,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
 // large-M configuration uses 128 x 128 wave tiles (0.5 KB per MFMA) to stay
 // clear of the LDS bandwidth.
 // --------------------------------------------------------------------------
-template <typename TA, int MTW, int NTW, int SKB_>
+template <typename TA, int MTW, int NTW, int SKB_, int NSTAGE_ = 3>
 struct TiledCfg {
   static constexpr int BM = 64 * MTW, BN = 64 * NTW;
   static constexpr int SKB = SKB_;                   // k-blocks (32 k) per stage
@@ -271,7 +271,7 @@ struct TiledCfg {
   static constexpr int NTB = BN / 16;                // packed n-tiles per block
   static constexpr int B_BYTES = SKB * NTB * 1024;
   static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int NSTAGE = 3;
+  static constexpr int NSTAGE = NSTAGE_;             // ring stages, NSTAGE - 1 in flight
   static constexpr int A_INST = A_BYTES / 1024, B_INST = SKB * NTB;
   static constexpr int LOADS = (A_INST + B_INST) / 4;  // DMA instructions per wave per stage
   static constexpr int EPI_BYTES = BM / 2 * BN * 4;  // the epilogue stages half the block tile at a time
@@ -350,9 +350,9 @@ __device__ inline void tiled_issue(const GemmArgs& g, unsigned char* st, int m0,
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-template <typename TA, int MTW, int NTW, int SKB>
+template <typename TA, int MTW, int NTW, int SKB, int NS>
 __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmArgs g) {
-  using C = TiledCfg<TA, MTW, NTW, SKB>;
+  using C = TiledCfg<TA, MTW, NTW, SKB, NS>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -644,7 +644,7 @@ static int ceil_div(int a, int b) { return (a + b - 1) / b; }
 // Column-tile counts per wave instantiated for the decode path.
 static const int kDecodeNT[] = {2, 4, 5, 8, 9, 10, 16};
 
-GemmPlan plan_gemm(int M, int K, int N, bool bf16, int n_cu) {
+GemmPlan plan_gemm(int M, int K, int N, bool bf16, bool a_f32, int n_cu) {
   GemmPlan g{};
   g.M = M; g.K = K; g.N = N;
   g.KB = bf16 ? Mfma<__bf16>::KB : Mfma<float>::KB;
@@ -683,9 +683,7 @@ GemmPlan plan_gemm(int M, int K, int N, bool bf16, int n_cu) {
   const bool big = M >= 256 && g.ntiles >= 64;  // 256 x 256 tiles, one k-block per stage
   if (bf16 && M > 16 && (big || g.kblocks % 2 == 0)) {
     // LDS-tiled kernel: 64 x 128 tiles up to 64 rows, 128 x 128 up to 255,
-    // 256 x 256 above; split K until there are two blocks per CU (slices a
-    // multiple of one stage), except that 256 x 256 tiles (one block per
-    // CU) only split when there are fewer blocks than about 0.8 CUs
+    // 256 x 256 above (one k-block per stage, slices a multiple of a stage)
     g.tiled = 1;
     g.MT = big ? 4 : (M > 64 ? 2 : 1);
     g.NT = big ? 4 : 2;
@@ -695,9 +693,35 @@ GemmPlan plan_gemm(int M, int K, int N, bool bf16, int n_cu) {
     g.gx = ceil_div(g.ntiles, NTB);
     g.gy = ceil_div(M, BM);
     const long blocks0 = (long)g.gx * g.gy;
-    const long want = big ? (long)(0.8 * n_cu) : 2L * n_cu;
     int ks = 1;
-    if (blocks0 < want) ks = (int)std::min<long>((want + blocks0 - 1) / blocks0, std::max(1, g.kblocks / 4));
+    if (big) {
+      // 256 x 256 tiles (one block per CU) only split K when there are
+      // fewer blocks than about 0.8 CUs
+      const long want = (long)(0.8 * n_cu);
+      if (blocks0 < want) ks = (int)std::min<long>((want + blocks0 - 1) / blocks0, std::max(1, g.kblocks / 4));
+    } else {
+      // Blocks run in rounds of n_cu * occ resident blocks (occ from the
+      // LDS ring); every round costs the streaming time of one block, a
+      // sparse last round as much as a full one.  Each K slice adds an fp32
+      // partial round trip.  A larger split must save 5% to be taken.
+      const int lds = a_f32 ? (g.MT == 2 ? TiledCfg<float, 2, 2, 2>::LDS : TiledCfg<float, 1, 2, 2, 4>::LDS)
+                            : (g.MT == 2 ? TiledCfg<__bf16, 2, 2, 2>::LDS : TiledCfg<__bf16, 1, 2, 2>::LDS);
+      const long slots = (long)n_cu * std::max(1, std::min(2, 160 * 1024 / lds));
+      const double kb_bytes = BM * 32.0 * (a_f32 ? 4 : 2) + NTB * 1024.0;  // one block, one k-block
+      double best_cost = 1e300;
+      for (int k = 1; k <= std::max(1, g.kblocks / (2 * skb)); ++k) {
+        const int kbs = ceil_div(ceil_div(g.kblocks, k), skb) * skb;
+        if (ceil_div(g.kblocks, kbs) != k) continue;
+        const long rounds = (blocks0 * k + slots - 1) / slots;
+        double cost = (double)rounds * kbs;  // k-blocks streamed by the busiest slot
+        // (partials: written, read back by a second launch; weighted double)
+        if (k > 1) cost += 2.0 * (double)k * M * g.Np * 8.0 / ((double)slots * kb_bytes);
+        if (cost < best_cost * 0.95) {
+          best_cost = cost;
+          ks = k;
+        }
+      }
+    }
     int kbs = ceil_div(g.kblocks, ks);
     kbs = ceil_div(kbs, skb) * skb;
     g.kb_per_split = kbs;
@@ -725,17 +749,17 @@ static hipError_t launch_gemm_t(const GemmPlan& g, const GemmArgs& a, hipStream_
   return hipGetLastError();
 }
 
-template <typename TA, int MTW, int NTW, int SKB>
+template <typename TA, int MTW, int NTW, int SKB, int NS = 3>
 static hipError_t launch_tiled_t(const GemmPlan& g, const GemmArgs& a, hipStream_t s) {
-  using C = TiledCfg<TA, MTW, NTW, SKB>;
+  using C = TiledCfg<TA, MTW, NTW, SKB, NS>;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_tiled_kernel<TA, MTW, NTW, SKB>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_tiled_kernel<TA, MTW, NTW, SKB, NS>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((gemm_tiled_kernel<TA, MTW, NTW, SKB>), dim3(g.gy, g.gx, g.ksplit), dim3(256), C::LDS, s, a);
+  hipLaunchKernelGGL((gemm_tiled_kernel<TA, MTW, NTW, SKB, NS>), dim3(g.gy, g.gx, g.ksplit), dim3(256), C::LDS, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || g.ksplit == 1) return e;
   const long total = (long)g.M * (g.Np / 2);
@@ -746,7 +770,10 @@ static hipError_t launch_tiled_t(const GemmPlan& g, const GemmArgs& a, hipStream
 template <typename TA>
 static hipError_t launch_tiled_sel(const GemmPlan& g, const GemmArgs& a, hipStream_t s) {
   if (g.MT == 4) return launch_tiled_t<TA, 4, 4, 1>(g, a, s);
-  return g.MT == 2 ? launch_tiled_t<TA, 2, 2, 2>(g, a, s) : launch_tiled_t<TA, 1, 2, 2>(g, a, s);
+  if (g.MT == 2) return launch_tiled_t<TA, 2, 2, 2>(g, a, s);
+  // fp32 A doubles the bytes per stage: one block per CU, so a fourth
+  // stage keeps three in flight
+  return sizeof(TA) == 4 ? launch_tiled_t<TA, 1, 2, 2, 4>(g, a, s) : launch_tiled_t<TA, 1, 2, 2>(g, a, s);
 }
 
 template <typename T, typename TA>

@@ -50,7 +50,8 @@ struct GemmPlan {
   size_t part_bytes; // fp32 partial tiles (ksplit > 1)
 };
 
-GemmPlan plan_gemm(int M, int K, int N, bool bf16, int n_cu);
+// a_f32: the A operand is fp32 (converted to bf16 fragments in the kernel)
+GemmPlan plan_gemm(int M, int K, int N, bool bf16, bool a_f32, int n_cu);
 
 // A is T (a_f32 == false) or fp32 (a_f32 == true); Wp is T.
 hipError_t launch_gemm(const GemmPlan& g, bool bf16, bool a_f32, const void* A, int lda, const void* Wp, float* part,
@@ -70,6 +71,7 @@ struct AttnArgs {
   const void* pool;
   const int32_t* page_table;
   int paged, page_size, n_pages, max_pages, s_max;
+  int tpp_shift;               // log2 of the 32-token tiles per page, -1 if not a power of two
   const int32_t* kv_len;
   int B, n_q, H, V;
   int n_hg, U;                 // head groups per query row; streams U = V * n_hg (set by the launcher)
