@@ -260,11 +260,13 @@ __device__ inline void issue_tile(const AttnArgs& a, unsigned char* stage, int b
   const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(gbase, nbytes);
   if constexpr (C::FAST) {
     // wave w fills rows 8w + lane/8 of every column block; dma_off holds the
-    // lane's row and swizzled chunk, block k adds 128 B in global memory
+    // lane's row and swizzled chunk, block k adds 128 B in global memory.
+    // Every cache row is read once per call (all heads share the tile):
+    // non-temporal loads (cache policy 2)
 #pragma unroll
     for (int kk = 0; kk < C::NINST / C::NW; ++kk)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, MLA_LDS_PTR(stage + (wave + 4 * kk) * 1024), 16,
-                                               dma_off + kk * 128, 0, 0, 0);
+                                               dma_off + kk * 128, 0, 0, 2);
   } else {
     // row-major rows; 16-byte chunk p of the tile goes to LDS byte 16 p
 #pragma unroll

@@ -138,10 +138,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     wp[ni] = reinterpret_cast<const T*>(g.Wp) + (size_t)nt * FR + lane * KPL;
   }
 
-  // Weights are read exactly once.  With fp32 activations (the output
-  // projection: its A operand is re-read by every column block) the weight
-  // stream uses non-temporal loads so that it does not evict A from L2.
-  constexpr bool kStreamW = sizeof(TA) == 4 && sizeof(frag) == 16;
+  // Weights are read exactly once: non-temporal loads (a read-once stream
+  // reaches a higher HBM rate that way, and does not evict the A operand,
+  // re-read by every column block, from L2).
+  constexpr bool kStreamW = sizeof(frag) == 16;
   auto load_b = [&](frag (&b)[NT], int kb) {
 #pragma unroll
     for (int ni = 0; ni < NT; ++ni) {
@@ -260,8 +260,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
 // large-M configuration uses 128 x 128 wave tiles (0.5 KB per MFMA) to stay
 // clear of the LDS bandwidth.
 // --------------------------------------------------------------------------
-template <typename TA, int MTW, int NTW, int SKB_, int NSTAGE_ = 3>
+template <typename TA, int MTW, int NTW, int SKB_, int NSTAGE_ = 3, bool WNT_ = false>
 struct TiledCfg {
+  static constexpr bool WNT = WNT_;                  // weights read once: non-temporal DMA
   static constexpr int BM = 64 * MTW, BN = 64 * NTW;
   static constexpr int SKB = SKB_;                   // k-blocks (32 k) per stage
   static constexpr int ESA = (int)sizeof(TA);
@@ -314,7 +315,8 @@ __device__ inline TiledDma<C> tiled_dma(const GemmArgs&, unsigned char* st, int 
 // (Not a template: the tile constants come in as arguments and fold at the
 // inlined call sites.)
 __device__ inline void tiled_dma_load(const GemmArgs& g, unsigned char* st, int m0, int nt0, int kb, bool live, int u,
-                                      int wave, int lane, int a_inst, int rowb, int esa, int ntb, int a_bytes) {
+                                      int wave, int lane, int a_inst, int rowb, int esa, int ntb, int a_bytes,
+                                      bool wnt) {
   const int aw = a_inst / 4, cpr = rowb / 16;
   if (u < aw) {
     // A: rows m0.., k from kb*32; the record count stops at row M (zeros below)
@@ -333,12 +335,18 @@ __device__ inline void tiled_dma_load(const GemmArgs& g, unsigned char* st, int 
     const int j = i / ntb, t = i % ntb;
     const int nt = nt0 + t;
     const int off = nt < g.ntiles ? (int)((((long)(kb + j) * g.ntiles) + nt) * 1024) + lane * 16 : 0x7ffffff0;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, MLA_LDS_PTR(st + a_bytes + i * 1024), 16, off, 0, 0, 0);
+    // (cache policy 2 = non-temporal: a stream read once reaches a higher
+    // HBM rate and does not displace A from L2)
+    if (wnt)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, MLA_LDS_PTR(st + a_bytes + i * 1024), 16, off, 0, 0, 2);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, MLA_LDS_PTR(st + a_bytes + i * 1024), 16, off, 0, 0, 0);
   }
 }
 template <class C>
 __device__ inline void tiled_dma_one(const GemmArgs& g, const TiledDma<C>& d, int u, int wave, int lane) {
-  tiled_dma_load(g, d.st, d.m0, d.nt0, d.kb, d.live, u, wave, lane, C::A_INST, C::ROWB, C::ESA, C::NTB, C::A_BYTES);
+  tiled_dma_load(g, d.st, d.m0, d.nt0, d.kb, d.live, u, wave, lane, C::A_INST, C::ROWB, C::ESA, C::NTB, C::A_BYTES,
+                 C::WNT);
 }
 template <class C>
 __device__ inline void tiled_issue(const GemmArgs& g, unsigned char* st, int m0, int nt0, int kb, bool live, int wave,
@@ -350,9 +358,9 @@ __device__ inline void tiled_issue(const GemmArgs& g, unsigned char* st, int m0,
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-template <typename TA, int MTW, int NTW, int SKB, int NS>
+template <typename TA, int MTW, int NTW, int SKB, int NS, bool WNT>
 __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmArgs g) {
-  using C = TiledCfg<TA, MTW, NTW, SKB, NS>;
+  using C = TiledCfg<TA, MTW, NTW, SKB, NS, WNT>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -749,17 +757,17 @@ static hipError_t launch_gemm_t(const GemmPlan& g, const GemmArgs& a, hipStream_
   return hipGetLastError();
 }
 
-template <typename TA, int MTW, int NTW, int SKB, int NS = 3>
+template <typename TA, int MTW, int NTW, int SKB, int NS = 3, bool WNT = false>
 static hipError_t launch_tiled_t(const GemmPlan& g, const GemmArgs& a, hipStream_t s) {
-  using C = TiledCfg<TA, MTW, NTW, SKB, NS>;
+  using C = TiledCfg<TA, MTW, NTW, SKB, NS, WNT>;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_tiled_kernel<TA, MTW, NTW, SKB, NS>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_tiled_kernel<TA, MTW, NTW, SKB, NS, WNT>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((gemm_tiled_kernel<TA, MTW, NTW, SKB, NS>), dim3(g.gy, g.gx, g.ksplit), dim3(256), C::LDS, s, a);
+  hipLaunchKernelGGL((gemm_tiled_kernel<TA, MTW, NTW, SKB, NS, WNT>), dim3(g.gy, g.gx, g.ksplit), dim3(256), C::LDS, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || g.ksplit == 1) return e;
   const long total = (long)g.M * (g.Np / 2);
@@ -770,10 +778,17 @@ static hipError_t launch_tiled_t(const GemmPlan& g, const GemmArgs& a, hipStream
 template <typename TA>
 static hipError_t launch_tiled_sel(const GemmPlan& g, const GemmArgs& a, hipStream_t s) {
   if (g.MT == 4) return launch_tiled_t<TA, 4, 4, 1>(g, a, s);
-  if (g.MT == 2) return launch_tiled_t<TA, 2, 2, 2>(g, a, s);
   // fp32 A doubles the bytes per stage: one block per CU, so a fourth
-  // stage keeps three in flight
-  return sizeof(TA) == 4 ? launch_tiled_t<TA, 1, 2, 2, 4>(g, a, s) : launch_tiled_t<TA, 1, 2, 2>(g, a, s);
+  // stage keeps three in flight.  With bf16 A and one row block the
+  // weights are read once: non-temporal weight DMA (measured slower with
+  // the fp32-A kernel, so not used there)
+  if constexpr (sizeof(TA) == 4) {
+    return g.MT == 2 ? launch_tiled_t<TA, 2, 2, 2>(g, a, s) : launch_tiled_t<TA, 1, 2, 2, 4>(g, a, s);
+  } else {
+    if (g.gy == 1)
+      return g.MT == 2 ? launch_tiled_t<TA, 2, 2, 2, 3, true>(g, a, s) : launch_tiled_t<TA, 1, 2, 2, 3, true>(g, a, s);
+    return g.MT == 2 ? launch_tiled_t<TA, 2, 2, 2>(g, a, s) : launch_tiled_t<TA, 1, 2, 2>(g, a, s);
+  }
 }
 
 template <typename T, typename TA>
