@@ -77,6 +77,21 @@ __device__ inline void epi_pair(const EpiArgs& e, int m, int n, float v0, float 
   dst[n + 1] = from_f32<T>(v1);
 }
 
+// XCD-aware block order: the hardware deals work-groups round-robin over the
+// 8 XCDs (each with its own L2), so physical block b runs on XCD b % 8.
+// Logical block (b % 8) * (T / 8) + b / 8 gives every XCD a contiguous range
+// of the (x fastest, then y, then z) logical order: one XCD then holds one
+// K slice (or two) of the A operand instead of all of them.
+struct BlockXYZ {
+  int x, y, z;
+};
+__device__ inline BlockXYZ xcd_block() {
+  const int gx = gridDim.x, gy = gridDim.y, T = gx * gy * gridDim.z;
+  const int b = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+  const int L = (T & 7) ? b : (b & 7) * (T >> 3) + (b >> 3);
+  return BlockXYZ{L % gx, (L / gx) % gy, L / (gx * gy)};
+}
+
 struct GemmArgs {
   const void* A;
   int lda;
@@ -103,10 +118,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int M = g.e.M;
-  const int col0 = blockIdx.x * COLS;                                  // first column of the block tile
-  const int nt0 = blockIdx.x * NGW * NT + (KSW == 1 ? wave * NT : 0);
-  const int mt0 = blockIdx.y * MT;
-  const int ks = blockIdx.z;
+  const BlockXYZ blk = xcd_block();
+  const int col0 = blk.x * COLS;                                       // first column of the block tile
+  const int nt0 = blk.x * NGW * NT + (KSW == 1 ? wave * NT : 0);
+  const int mt0 = blk.y * MT;
+  const int ks = blk.z;
   int kb0 = ks * g.kb_per_split;
   int kb1 = min(kb0 + g.kb_per_split, g.kblocks);
   if (KSW > 1) {  // this wave's share of the slice
@@ -367,8 +383,9 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmArgs g) {
   const int wm = wave & 1, wn = wave >> 1;
   // row blocks vary fastest: blocks running together share their weight
   // columns (each W tile is fetched once) while A, M rows deep, stays cached
-  const int m0 = blockIdx.x * C::BM, nt0 = blockIdx.y * C::NTB;
-  const int ks = blockIdx.z;
+  const BlockXYZ blk = xcd_block();
+  const int m0 = blk.x * C::BM, nt0 = blk.y * C::NTB;
+  const int ks = blk.z;
   const int kb0 = ks * g.kb_per_split, kb1 = min(kb0 + g.kb_per_split, g.kblocks);
   const int nst = (kb1 - kb0 + C::SKB - 1) / C::SKB;  // stages in this slice
 
