@@ -192,9 +192,6 @@ mla_status attention_impl(const mla_dims* d, const WsLayout& W, const void* q, c
   a.page_table = c->page_table;
   a.paged = c->page_table != nullptr;
   a.page_size = a.paged ? c->page_size : 32;
-  a.tpp_shift = -1;
-  for (int sh = 0; sh < 31; ++sh)
-    if ((32 << sh) == a.page_size) a.tpp_shift = sh;
   a.n_pages = c->n_pages;
   a.max_pages = c->max_pages_per_seq;
   a.s_max = c->s_max;

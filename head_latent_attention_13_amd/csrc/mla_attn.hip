@@ -129,8 +129,10 @@ __device__ inline void o_settle(f32x16 (&O)[NTH][NCT]) {
   }
 }
 
-template <typename T_, int HP_, int NW_, int DL_, int DR_, int NSTAGE_>
+template <typename T_, int HP_, int NW_, int DL_, int DR_, int NSTAGE_, bool CNT_ = false>
 struct AttnCfg {
+  // cache rows read by one stream only: non-temporal tile loads
+  static constexpr bool CNT = CNT_;
   using T = T_;
   using F = Mfma32<T>;
   static constexpr int HP = HP_, NW = NW_, DL = DL_, DR = DR_, R = DL_ + DR_;
@@ -176,6 +178,7 @@ struct AttnCfg {
 // latent columns (PV phase); the fp32 O accumulators (128 x 512) fill the
 // AGPRs of the four waves.
 using CfgBf16 = AttnCfg<__bf16, 128, 4, 512, 64, 3>;
+using CfgBf16Nt = AttnCfg<__bf16, 128, 4, 512, 64, 3, true>;
 using CfgF32 = AttnCfg<float, 32, 1, 32, 8, 3>;
 
 // Softmax statistics are only rebased when a head's running max grows by
@@ -222,19 +225,6 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) 
   return __builtin_amdgcn_make_buffer_rsrc(b, (short)0, __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
-// Page holding tile k of sequence b (paged caches, 32-token tiles): the
-// work-group keeps a window of the page table in a VGPR (lane j holds the
-// entry of page wp0 + j, loaded once per segment), so the tile loop reads
-// page ids with a lane read instead of a scalar load (whose wait would also
-// drain every outstanding LDS access of the wave); pages outside the window
-// are read from the table.
-__device__ inline int tile_page(const AttnArgs& a, int b, int k, int pgw, int wp0) {
-  const int pidx = a.tpp_shift >= 0 ? (k >> a.tpp_shift) : k / (a.page_size >> 5);
-  const int j = pidx - wp0;
-  if (j >= 0 && j < 64) return __builtin_amdgcn_readlane(pgw, j);
-  return MLA_CONST_PTR(a.page_table)[(size_t)b * a.max_pages + pidx];
-}
-
 // DMA one 32-row tile into an LDS stage with buffer loads whose record
 // count is the tile's visible bytes: rows at or past `vis`, a page id
 // outside the pool (which also raises error bit 2), and a tile past the end
@@ -242,13 +232,13 @@ __device__ inline int tile_page(const AttnArgs& a, int b, int k, int pgw, int wp
 // so the pipeline can wait on a constant count.
 template <class C>
 __device__ inline void issue_tile(const AttnArgs& a, unsigned char* stage, int b, int k, int vis, int wave,
-                                  int lane, int dma_off, bool live, int pgw, int wp0) {
+                                  int lane, int dma_off, bool live) {
   const int t0 = k * C::TILE;
   const unsigned char* gbase = reinterpret_cast<const unsigned char*>(a.pool);
   bool ok = live;
   if (live) {
     if (a.paged) {
-      const int pg = tile_page(a, b, k, pgw, wp0);
+      const int pg = MLA_CONST_PTR(a.page_table)[(size_t)b * a.max_pages + t0 / a.page_size];
       ok = (pg >= 0) && (pg < a.n_pages);
       if (!ok && lane == 0) atomicOr(a.err, 2);  // flagged, then read as zeros
       gbase += ((size_t)(ok ? pg : 0) * a.page_size + (t0 % a.page_size)) * (size_t)C::ROW_BYTES;
@@ -261,12 +251,21 @@ __device__ inline void issue_tile(const AttnArgs& a, unsigned char* stage, int b
   if constexpr (C::FAST) {
     // wave w fills rows 8w + lane/8 of every column block; dma_off holds the
     // lane's row and swizzled chunk, block k adds 128 B in global memory.
-    // Every cache row is read once per call (all heads share the tile):
-    // non-temporal loads (cache policy 2)
+    // When every cache row is read by one stream only (one query token, all
+    // heads in one work-group: C::CNT) the loads are non-temporal (cache
+    // policy 2); with several query tokens per sequence the tiles are
+    // re-read by the other streams and stay cacheable.
+    if constexpr (C::CNT) {
 #pragma unroll
-    for (int kk = 0; kk < C::NINST / C::NW; ++kk)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, MLA_LDS_PTR(stage + (wave + 4 * kk) * 1024), 16,
-                                               dma_off + kk * 128, 0, 0, 2);
+      for (int kk = 0; kk < C::NINST / C::NW; ++kk)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, MLA_LDS_PTR(stage + (wave + 4 * kk) * 1024), 16,
+                                                 dma_off + kk * 128, 0, 0, 2);
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < C::NINST / C::NW; ++kk)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, MLA_LDS_PTR(stage + (wave + 4 * kk) * 1024), 16,
+                                                 dma_off + kk * 128, 0, 0, 0);
+    }
   } else {
     // row-major rows; 16-byte chunk p of the tile goes to LDS byte 16 p
 #pragma unroll
@@ -311,12 +310,12 @@ __device__ __forceinline__ void tile_step(const AttnArgs& a, unsigned char* __re
                                           int b, int k_issue, int tok0, int vis, int i, int wave, int lane,
                                           int dma_off, const int (&s_base)[4], const int (&tr_base)[2][2],
                                           const typename C::F::frag (&qf)[C::RKQ], float& m_run, float& l_run,
-                                          f32x16 (&O)[C::NTH][C::NCT], int pgw, int wp0) {
+                                          f32x16 (&O)[C::NTH][C::NCT]) {
   using T = typename C::T;
   using F = typename C::F;
   using frag = typename F::frag;
   const int hi = lane >> 5, l32 = lane & 31;
-  issue_tile<C>(a, dma_stage, b, k_issue, vis, wave, lane, dma_off, issue, pgw, wp0);
+  issue_tile<C>(a, dma_stage, b, k_issue, vis, wave, lane, dma_off, issue);
 
   // ---- S^T[32 tokens x 32 heads] = tile . q^T (one MFMA chain) --------
   auto a_frag = [&](int kb) -> frag {
@@ -567,15 +566,9 @@ __global__ __launch_bounds__(C::NTHR, 1) void attn_split_kernel(AttnArgs a) {
     const int h_base = hgrp * C::HP;
     const int b = v / a.n_q;
 
-    // page-table window of the segment (paged caches)
-    int pgw = -1, wp0 = 0;
-    if (a.paged) {
-      wp0 = a.tpp_shift >= 0 ? (k0 >> a.tpp_shift) : k0 / (a.page_size >> 5);
-      if (wp0 + lane < a.max_pages) pgw = a.page_table[(size_t)b * a.max_pages + wp0 + lane];
-    }
     // tile 0 first, then q, then the other prologue tiles: the wait before
     // tile 0 then also covers q, and later tiles stay in flight
-    issue_tile<C>(a, smem, b, k0, vis, wave, lane, dma_off, true, pgw, wp0);
+    issue_tile<C>(a, smem, b, k0, vis, wave, lane, dma_off, true);
     asm volatile("" ::: "memory");  // keep the issue order: tile 0, q, tile 1
     // q^T fragments of this wave's 32 heads: the first RKQ k-steps in
     // registers, the trailing QL column blocks DMA'd into LDS (same
@@ -592,7 +585,7 @@ __global__ __launch_bounds__(C::NTHR, 1) void attn_split_kernel(AttnArgs a) {
     }
     asm volatile("" ::: "memory");
     for (int s = 1; s < C::NSTAGE - 1; ++s)
-      issue_tile<C>(a, smem + s * C::TILE_BYTES, b, k0 + s, vis, wave, lane, dma_off, s < cnt, pgw, wp0);
+      issue_tile<C>(a, smem + s * C::TILE_BYTES, b, k0 + s, vis, wave, lane, dma_off, s < cnt);
 
     float m_run = -1e30f, l_run = 0.f;
     f32x16 O[C::NTH][C::NCT];
@@ -608,7 +601,7 @@ __global__ __launch_bounds__(C::NTHR, 1) void attn_split_kernel(AttnArgs a) {
       tile_step<C>(a, smem + ((i + C::NSTAGE - 1) % C::NSTAGE) * C::TILE_BYTES, smem + (i % C::NSTAGE) * C::TILE_BYTES,
                    p_s, smem + C::OFF_Q + wave * 4096, alpha_s, flag_s, i + C::NSTAGE - 1 < cnt, b,
                    k0 + i + C::NSTAGE - 1, (k0 + i) * C::TILE, vis, i, wave, lane, dma_off, s_base, tr_base, qf, m_run,
-                   l_run, O, pgw, wp0);
+                   l_run, O);
     };
     // tile 0 is peeled: the compiler's wait for the q registers then lands
     // in front of its first use (leaving the DMA of tile 1 in flight)
@@ -937,7 +930,10 @@ hipError_t launch_attention(const AttnArgs& a_in, bool bf16, hipStream_t s) {
   a.wrec = a.sched;
   a.srec = a.wrec + 8 * a.G;
   a.wfl = a.srec + 4 * a.U;
-  return bf16 ? launch_attn_t<CfgBf16>(a, s) : launch_attn_t<CfgF32>(a, s);
+  if (!bf16) return launch_attn_t<CfgF32>(a, s);
+  // one query token and one head group: every cache row is read by one
+  // stream only, so its tiles are loaded non-temporally
+  return (a.n_q == 1 && a.n_hg == 1) ? launch_attn_t<CfgBf16Nt>(a, s) : launch_attn_t<CfgBf16>(a, s);
 }
 
 }  // namespace mla

@@ -666,8 +666,10 @@ __global__ __launch_bounds__(256) void splitk_epilogue_kernel(GemmArgs g) {
 
 static int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-// Column-tile counts per wave instantiated for the decode path.
-static const int kDecodeNT[] = {2, 4, 5, 8, 9, 10, 16};
+// Column-tile counts per wave instantiated for the decode path (16 tiles
+// per wave, one wave per SIMD, measured slower than 10 in every split
+// tried for the output projection).
+static const int kDecodeNT[] = {2, 4, 5, 8, 9, 10};
 
 GemmPlan plan_gemm(int M, int K, int N, bool bf16, bool a_f32, int n_cu) {
   GemmPlan g{};
@@ -679,8 +681,10 @@ GemmPlan plan_gemm(int M, int K, int N, bool bf16, bool a_f32, int n_cu) {
   g.ntiles = g.Np / 16;
   const int mtiles = ceil_div(std::max(M, 1), 16);
   // Cost model for a weight-streaming kernel (units: 1 KB fragments): the
-  // busiest CU streams ceil(blocks / CUs) blocks of cols * kb_per_split
-  // fragments; fewer than two blocks per CU leave too few loads in flight;
+  // busiest CU streams ceil(blocks / CUs) blocks of (cols + A) * kb_per_split
+  // fragments; fewer than two narrow blocks per CU leave too few loads in
+  // flight (measured: wide blocks, 10 column tiles per wave, do best at one
+  // block per CU);
   // every K slice beyond the first adds an fp32 partial round trip and a
   // second launch.
   double best = 1e300;
@@ -693,9 +697,13 @@ GemmPlan plan_gemm(int M, int K, int N, bool bf16, bool a_f32, int n_cu) {
       const int kbs = ceil_div(g.kblocks, ks);
       if (ceil_div(g.kblocks, kbs) != ks) continue;
       const long blocks = (long)gx * gy * ks;
-      double cost = (double)((blocks + n_cu - 1) / n_cu) * cols * kbs;
+      // per k-block a block streams `cols` weight fragments; an fp32 A
+      // operand (the output projection's, large and re-read by every column
+      // block) adds its fragments too, once per wave covering the k-block
+      const double a_kb = a_f32 ? 2.0 * MT * (KSW == 1 ? 4 : 1) : 0.0;
+      double cost = (double)((blocks + n_cu - 1) / n_cu) * (cols + a_kb) * kbs;
       if (blocks < n_cu) cost *= 1.6;
-      else if (blocks < 2L * n_cu) cost *= 1.25;
+      else if (blocks < 2L * n_cu && NT < 8) cost *= 1.25;  // narrow blocks: few loads in flight
       if (ks > 1) cost += 2.0 * ks * M * g.Np * 4.0 / 1024.0 / n_cu + 100.0;
       if (cost < best * 0.999 || (cost <= best * 1.001 && blocks < best_blocks)) {
         best = cost;
@@ -817,8 +825,7 @@ static hipError_t launch_gemm_sel(const GemmPlan& g, const GemmArgs& a, hipStrea
       case 5: return launch_gemm_t<T, TA, 1, 5, 4>(g, a, s);
       case 8: return launch_gemm_t<T, TA, 1, 8, 4>(g, a, s);
       case 9: return launch_gemm_t<T, TA, 1, 9, 4>(g, a, s);
-      case 10: return launch_gemm_t<T, TA, 1, 10, 4>(g, a, s);
-      default: return launch_gemm_t<T, TA, 1, 16, 4>(g, a, s);
+      default: return launch_gemm_t<T, TA, 1, 10, 4>(g, a, s);
     }
   }
   if (g.KSW == 4 && g.MT == 2) {

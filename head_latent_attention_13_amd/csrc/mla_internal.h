@@ -71,7 +71,6 @@ struct AttnArgs {
   const void* pool;
   const int32_t* page_table;
   int paged, page_size, n_pages, max_pages, s_max;
-  int tpp_shift;               // log2 of the 32-token tiles per page, -1 if not a power of two
   const int32_t* kv_len;
   int B, n_q, H, V;
   int n_hg, U;                 // head groups per query row; streams U = V * n_hg (set by the launcher)
