@@ -246,6 +246,8 @@ def test_v3_chunked_prefill_causal():
     ([1, 95, 200], 1),
     ([0, 40], 5),             # causal inside a small chunk, from an empty cache
     ([70], 33),               # chunk crossing tile boundaries
+    ([10, 50, 90, 130], 25),  # 100 token rows: 128-row GEMM tiles, one row block
+    ([3, 17, 40, 64, 90, 111, 150, 199], 25),  # 200 rows: two row blocks share weight tiles
 ])
 def test_edge_lengths(lengths, n_q):
     cfg = config(1).with_(batch=len(lengths), cached=0, n_q=n_q, name=f"edge{lengths}x{n_q}")
