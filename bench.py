@@ -38,6 +38,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--config", type=int, default=1, help="workload index (1: V2 decode, B=16 x 4096)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copies", type=int, default=4,
+                   help="input sets (absorbed weights, cache, activations) rotated over the steps, so that no "
+                        "step finds its inputs in the 256 MB last-level cache")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget for the oracle sample")
     p.add_argument("--copy-calib-mb", type=int, default=0,
                    help="only run a plain device copy of this many MB (counter calibration)")
@@ -168,6 +171,8 @@ def main():
     t_abs1.record()
     torch.cuda.synchronize()
     absorb_ms = t_abs0.elapsed_time(t_abs1)
+    NC = max(1, args.copies)
+    layers = [layer] + [mla.MLALayer(dims, raw, max_batch=B, max_nq=n_q) for _ in range(NC - 1)]
     del raw
 
     kv_len = case.cached + n_q
@@ -191,35 +196,47 @@ def main():
     x = devt(case.x_new.reshape(B * n_q, cfg.d_model))
     pos = torch.from_numpy(case.cached.astype(np.int32)).cuda()
     kv = torch.from_numpy(kv_len.astype(np.int32)).cuda()
-    q = torch.empty(B * n_q, H, R, dtype=tdt, device="cuda")
-    o_lat = torch.empty(B * n_q, H, cfg.d_latent, dtype=torch.float32, device="cuda")
-    y = torch.empty(B * n_q, cfg.d_model, dtype=torch.float32, device="cuda")
+    # copy j of every input: step k runs on copy k % NC
+    if cfg.paged:
+        caches = [cache] + [mla.Cache(pool=pool.clone(), page_table=table.clone(), page_size=cache.page_size,
+                                      n_pages=cache.n_pages, max_pages_per_seq=cache.max_pages_per_seq)
+                            for _ in range(NC - 1)]
+    else:
+        caches = [cache] + [mla.Cache(pool=pool.clone(), s_max=cache.s_max) for _ in range(NC - 1)]
+    xs = [x] + [x.clone() for _ in range(NC - 1)]
+    poss = [pos] + [pos.clone() for _ in range(NC - 1)]
+    kvs = [kv] + [kv.clone() for _ in range(NC - 1)]
+    qs = [torch.empty(B * n_q, H, R, dtype=tdt, device="cuda") for _ in range(NC)]
+    o_lats = [torch.empty(B * n_q, H, cfg.d_latent, dtype=torch.float32, device="cuda") for _ in range(NC)]
+    ys = [torch.empty(B * n_q, cfg.d_model, dtype=torch.float32, device="cuda") for _ in range(NC)]
 
     calls = ("mla_compress_append", "mla_q_proj", "mla_attention", "mla_out_proj")
 
-    def step(evs=None):
+    def step(k, evs=None):
         def mark(i):
             if evs is not None:
                 evs[i].record()
+        j = k % NC
+        ly, cc, xx, qq, ol = layers[j], caches[j], xs[j], qs[j], o_lats[j]
         mark(0)
-        layer.append(x, pos, B, n_q, cache)
+        ly.append(xx, poss[j], B, n_q, cc)
         mark(1)
-        layer.q_proj(x, kv, B, n_q, q)
+        ly.q_proj(xx, kvs[j], B, n_q, qq)
         mark(2)
-        layer.attention(q, kv, B, n_q, cache, o_lat)
+        ly.attention(qq, kvs[j], B, n_q, cc, ol)
         mark(3)
-        layer.out_proj(o_lat, B * n_q, y)
+        ly.out_proj(ol, B * n_q, ys[j])
         mark(4)
 
-    for _ in range(args.warmup):
-        step()
+    for k in range(args.warmup):
+        step(k)
     torch.cuda.synchronize()
     # timed region: K whole steps back to back, events only at its ends
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     t_start.record()
     for k in range(args.steps):
-        step()
+        step(k)
     t_end.record()
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
@@ -229,11 +246,11 @@ def main():
     # not used for the step time)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     for k in range(args.steps):
-        step(ev[k])
+        step(k, ev[k])
     torch.cuda.synchronize()
     per_call_ms = {c: float(np.mean([ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(args.steps)]))
                    for i, c in enumerate(calls)}
-    assert layer.device_error() == 0
+    assert all(ly.device_error() == 0 for ly in layers)
 
     # ---- algorithmic bytes / flops per call (one step) ------------------
     eb = 2 if cfg.dtype == "bf16" else 4
