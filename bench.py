@@ -38,6 +38,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--config", type=int, default=1, help="workload index (1: V2 decode, B=16 x 4096)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--form", choices=("merged", "factored"), default="merged",
+                   help="absorbed weights: merged products (default) or the factors applied at run time")
     p.add_argument("--copies", type=int, default=4,
                    help="input sets (absorbed weights, cache, activations) rotated over the steps, so that no "
                         "step finds its inputs in the 256 MB last-level cache")
@@ -159,7 +161,7 @@ def main():
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     devt = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda().to(tdt)
     dims = mla.make_dims(cfg.d_model, H, cfg.d_latent, cfg.d_q_latent, cfg.d_nope, cfg.d_rope, cfg.d_v,
-                         cfg.dtype, cfg.rope_base)
+                         cfg.dtype, cfg.rope_base, form=args.form)
     raw = {k: devt(v) for k, v in case.weights.items()}
 
     # one-time absorption, timed on its own
@@ -269,6 +271,15 @@ def main():
         "mla_out_proj": {"bytes": wbytes[3] + M * H * cfg.d_latent * 4 + M * cfg.d_model * 4,
                          "flops": 2 * M * H * cfg.d_latent * cfg.d_model},
     }
+    if args.form == "factored":
+        # the factors plus the intermediates c_Q W_UQ and o_lat W_UV (written, read back)
+        algo["mla_q_proj"] = {
+            "bytes": wbytes[1] + wbytes[2] + M * cfg.d_model * eb + M * H * R * eb + 2 * M * H * cfg.d_nope * eb,
+            "flops": 2 * M * (cfg.d_model * cfg.d_q_latent + cfg.d_q_latent * H * (cfg.d_nope + cfg.d_rope)
+                              + H * cfg.d_nope * cfg.d_latent)}
+        algo["mla_out_proj"] = {
+            "bytes": wbytes[3] + M * H * cfg.d_latent * 4 + M * cfg.d_model * 4 + 2 * M * H * cfg.d_v * eb,
+            "flops": 2 * M * H * cfg.d_v * (cfg.d_latent + cfg.d_model)}
     mfma_peak = BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else F32_PEAK_TFLOPS
     kernels = {}
     for c in calls:
@@ -309,7 +320,8 @@ def main():
         "config": {"workload": cfg.name, "batch": B, "cached_tokens": (list(cfg.cached) if isinstance(cfg.cached, tuple)
                                                                       else int(cfg.cached)),
                    "new_tokens": n_q, "heads": H, "d_latent": cfg.d_latent, "d_rope": cfg.d_rope,
-                   "d_model": cfg.d_model, "cache": "paged" if cfg.paged else "contiguous"},
+                   "d_model": cfg.d_model, "cache": "paged" if cfg.paged else "contiguous",
+                   "weights": args.form},
         "roofline": roofline,
         "latent_cache_GB_s": round(cache_bytes / (per_call_ms["mla_attention"] * 1e-3) / 1e9, 1),
         "attention_mfma_pct": round(100 * att["mfma_frac"], 2),

@@ -4,13 +4,13 @@ The compute lives in libmla.so (hand-written HIP for gfx950, C ABI in
 include/mla.h); this package is its thin ctypes binding plus a small helper
 that owns the device buffers of one layer (``MLALayer``).
 """
-from ._lib import (MLA_BF16, MLA_F32, RAW_WEIGHT_NAMES, Cache, MLAError, EXPORTED, LIB_PATH, load, make_dims,
+from ._lib import (MLA_BF16, MLA_F32, MLA_WEIGHTS_FACTORED, MLA_WEIGHTS_MERGED, RAW_WEIGHT_NAMES, Cache, MLAError, EXPORTED, LIB_PATH, load, make_dims,
                    mla_absorb_weights, mla_absorbed_layout, mla_attention, mla_compress_append, mla_decode,
                    mla_dims, mla_out_proj, mla_q_proj, mla_read_device_error, mla_version, mla_workspace_size)
 from .layer import MLALayer
 
 __all__ = [
-    "MLA_BF16", "MLA_F32", "RAW_WEIGHT_NAMES", "Cache", "MLAError", "EXPORTED", "LIB_PATH", "load", "make_dims",
+    "MLA_BF16", "MLA_F32", "MLA_WEIGHTS_FACTORED", "MLA_WEIGHTS_MERGED", "RAW_WEIGHT_NAMES", "Cache", "MLAError", "EXPORTED", "LIB_PATH", "load", "make_dims",
     "mla_absorb_weights", "mla_absorbed_layout", "mla_attention", "mla_compress_append", "mla_decode",
     "mla_dims", "mla_out_proj", "mla_q_proj", "mla_read_device_error", "mla_version", "mla_workspace_size",
     "MLALayer",

@@ -20,6 +20,8 @@ LIB_PATH = os.path.join(_PKG, "libmla.so")
 
 MLA_F32 = 0
 MLA_BF16 = 1
+MLA_WEIGHTS_MERGED = 0
+MLA_WEIGHTS_FACTORED = 1
 
 RAW_WEIGHT_NAMES = ("W_DQ", "W_UQ", "W_QR", "W_DKV", "W_KR", "W_UK", "W_UV", "W_O")
 
@@ -34,7 +36,7 @@ class mla_dims(ctypes.Structure):
     _fields_ = [("d_model", ctypes.c_int32), ("n_heads", ctypes.c_int32), ("d_latent", ctypes.c_int32),
                 ("d_q_latent", ctypes.c_int32), ("d_nope", ctypes.c_int32), ("d_rope", ctypes.c_int32),
                 ("d_v", ctypes.c_int32), ("dtype", ctypes.c_int32), ("rope_base", ctypes.c_float),
-                ("softmax_scale", ctypes.c_float)]
+                ("softmax_scale", ctypes.c_float), ("weight_form", ctypes.c_int32)]
 
 
 class mla_raw_weights(ctypes.Structure):
@@ -112,9 +114,10 @@ def _stream(stream) -> ctypes.c_void_p:
 
 
 def make_dims(d_model, n_heads, d_latent, d_q_latent, d_nope, d_rope, d_v, dtype, rope_base=10000.0,
-              softmax_scale=0.0) -> mla_dims:
+              softmax_scale=0.0, form="merged") -> mla_dims:
     dt = {"f32": MLA_F32, "bf16": MLA_BF16, MLA_F32: MLA_F32, MLA_BF16: MLA_BF16}[dtype]
-    return mla_dims(d_model, n_heads, d_latent, d_q_latent, d_nope, d_rope, d_v, dt, rope_base, softmax_scale)
+    wf = {"merged": MLA_WEIGHTS_MERGED, "factored": MLA_WEIGHTS_FACTORED}[form]
+    return mla_dims(d_model, n_heads, d_latent, d_q_latent, d_nope, d_rope, d_v, dt, rope_base, softmax_scale, wf)
 
 
 @dataclass

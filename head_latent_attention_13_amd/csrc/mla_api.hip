@@ -60,8 +60,20 @@ mla_status check_dims(const mla_dims* d) {
   const int KB = is_bf16(d) ? 32 : 4;
   if (d->d_model % KB || d->d_q_latent % KB || (d->n_heads * d->d_latent) % KB)
     return fail(MLA_ERR_UNSUPPORTED, "d_model, d_q_latent and n_heads*d_latent must be multiples of %d", KB);
+  if (d->weight_form != MLA_WEIGHTS_MERGED && d->weight_form != MLA_WEIGHTS_FACTORED)
+    return fail(MLA_ERR_INVALID_ARG, "weight_form %d", d->weight_form);
+  if (d->weight_form == MLA_WEIGHTS_FACTORED) {
+    // reduction widths of the run-time factors, and whole 16-column tiles
+    // per head for the per-head products
+    if (d->d_nope % KB || d->d_latent % KB || (d->n_heads * d->d_v) % KB)
+      return fail(MLA_ERR_UNSUPPORTED, "factored weights: d_nope, d_latent and n_heads*d_v must be multiples of %d", KB);
+    if (d->d_latent % 16 || d->d_v % 16)
+      return fail(MLA_ERR_UNSUPPORTED, "factored weights: d_latent and d_v must be multiples of 16");
+  }
   return MLA_OK;
 }
+
+bool factored(const mla_dims* d) { return d->weight_form == MLA_WEIGHTS_FACTORED; }
 
 mla_status check_attn_dims(const mla_dims* d) {
   if (!attn_supported(is_bf16(d), d->n_heads, d->d_latent, d->d_rope))
@@ -78,28 +90,53 @@ float scale_of(const mla_dims* d) {
 // ---------------------------------------------------------- absorbed ----
 struct AbsLayout {
   size_t off[4], bytes[4], total;
+  // factored form: byte offsets of W_UQ, W_QR, W_UKT (region 2), W_UV, W_O (region 3)
+  size_t uq, qr, ukt, uv, wo;
 };
 
+size_t packed_bytes(const mla_dims* d, int K, int N) {
+  const int KB = is_bf16(d) ? 32 : 4;
+  return (size_t)ceil_div(K, KB) * KB * (size_t)ceil_div(N, 16) * 16 * esize(d);
+}
+
 AbsLayout abs_layout(const mla_dims* d) {
-  const int KB = is_bf16(d) ? 32 : 4, R = row_width(d);
-  const int K[4] = {d->d_model, d->d_model, d->d_q_latent, d->n_heads * d->d_latent};
-  const int N[4] = {R, d->d_q_latent, d->n_heads * R, d->d_model};
+  const int R = row_width(d), H = d->n_heads;
   AbsLayout L{};
   size_t o = 0;
-  for (int i = 0; i < 4; ++i) {
-    L.off[i] = o;
-    L.bytes[i] = (size_t)ceil_div(K[i], KB) * KB * (size_t)ceil_div(N[i], 16) * 16 * esize(d);
-    o = align256(o + L.bytes[i]);
+  auto put = [&](int K, int N) {
+    const size_t at = o;
+    o = align256(o + packed_bytes(d, K, N));
+    return at;
+  };
+  L.off[0] = put(d->d_model, R);
+  L.off[1] = put(d->d_model, d->d_q_latent);
+  L.off[2] = o;
+  if (!factored(d)) {
+    put(d->d_q_latent, H * R);
+    L.off[3] = o;
+    put(H * d->d_latent, d->d_model);
+  } else {
+    L.uq = put(d->d_q_latent, H * d->d_nope);
+    L.qr = put(d->d_q_latent, H * d->d_rope);
+    L.ukt = put(d->d_nope, H * d->d_latent);
+    L.off[3] = o;
+    L.uv = put(d->d_latent, H * d->d_v);
+    L.wo = put(H * d->d_v, d->d_model);
   }
   L.total = o;
+  for (int i = 0; i < 4; ++i) L.bytes[i] = (i < 3 ? L.off[i + 1] : L.total) - L.off[i];
   return L;
 }
 
 // ---------------------------------------------------------- workspace ----
 struct WsLayout {
-  size_t err, q, cq, part, tile_off, attn_o, attn_lse, total;
+  size_t err, q, cq, qn, vo, part, tile_off, attn_o, attn_lse, total;
   GemmPlan g_app, g_cq, g_q, g_out;
+  // factored form: q_nope = c_Q W_UQ, q_pe, q_lat = q_nope[h] W_UK[h]^T,
+  // v = o_lat[h] W_UV[h], y = v W_O
+  GemmPlan g_qn, g_qr, g_qk, g_ov, g_oo;
   int G, V;
+  bool plans_ok;
 };
 
 WsLayout ws_layout(const mla_dims* d, int batch, int n_q) {
@@ -109,15 +146,32 @@ WsLayout ws_layout(const mla_dims* d, int batch, int n_q) {
   const int ncu = device_cus();
   W.g_app = plan_gemm(M, d->d_model, R, bf, false, ncu);
   W.g_cq = plan_gemm(M, d->d_model, d->d_q_latent, bf, false, ncu);
-  W.g_q = plan_gemm(M, d->d_q_latent, H * R, bf, false, ncu);
-  W.g_out = plan_gemm(M, H * d->d_latent, d->d_model, bf, true, ncu);
+  size_t part = std::max(W.g_app.part_bytes, W.g_cq.part_bytes);
+  if (!factored(d)) {
+    W.g_q = plan_gemm(M, d->d_q_latent, H * R, bf, false, ncu);
+    W.g_out = plan_gemm(M, H * d->d_latent, d->d_model, bf, true, ncu);
+    part = std::max(part, std::max(W.g_q.part_bytes, W.g_out.part_bytes));
+    W.plans_ok = true;
+  } else {
+    W.g_qn = plan_gemm(M, d->d_q_latent, H * d->d_nope, bf, false, ncu);
+    W.g_qr = plan_gemm(M, d->d_q_latent, H * d->d_rope, bf, false, ncu);
+    // per-head products: head h's output tiles read A columns h*K ..
+    W.g_qk = plan_gemm(M, d->d_nope, H * d->d_latent, bf, false, ncu, d->d_latent / 16, d->d_nope);
+    W.g_ov = plan_gemm(M, d->d_latent, H * d->d_v, bf, true, ncu, d->d_v / 16, d->d_latent);
+    W.g_oo = plan_gemm(M, H * d->d_v, d->d_model, bf, false, ncu);
+    for (const GemmPlan* g : {&W.g_qn, &W.g_qr, &W.g_qk, &W.g_ov, &W.g_oo}) part = std::max(part, g->part_bytes);
+    W.plans_ok = W.g_qk.tiled >= 0 && W.g_ov.tiled >= 0;
+  }
   W.G = ncu;
   W.V = M;
   size_t o = 0;
   W.err = o; o = align256(o + 256);
   W.q = o; o = align256(o + (size_t)M * H * R * esize(d));
   W.cq = o; o = align256(o + (size_t)M * d->d_q_latent * esize(d));
-  size_t part = std::max(std::max(W.g_app.part_bytes, W.g_cq.part_bytes), std::max(W.g_q.part_bytes, W.g_out.part_bytes));
+  if (factored(d)) {
+    W.qn = o; o = align256(o + (size_t)M * H * d->d_nope * esize(d));
+    W.vo = o; o = align256(o + (size_t)M * H * d->d_v * esize(d));
+  }
   W.part = o; o = align256(o + part);
 
   const int HG = attn_head_group(bf);
@@ -131,6 +185,7 @@ WsLayout ws_layout(const mla_dims* d, int batch, int n_q) {
 }
 
 mla_status check_ws(const WsLayout& W, void* ws, size_t ws_bytes) {
+  if (!W.plans_ok) return fail(MLA_ERR_UNSUPPORTED, "no GEMM configuration fits the per-head factored products");
   if (!ws) return fail(MLA_ERR_INVALID_ARG, "workspace is NULL");
   if (!aligned(ws, 256)) return fail(MLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   if (ws_bytes < W.total) return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, W.total);
@@ -179,7 +234,27 @@ mla_status q_proj_impl(const mla_dims* d, const WsLayout& W, const unsigned char
   EpiArgs e = base_epi(EPI_Q, q);
   e.d_latent = d->d_latent; e.d_rope = d->d_rope; e.row = row_width(d); e.rope_base = d->rope_base;
   e.n_q = n_q; e.kv_len = kv_len;
-  st = run_gemm(W, G_Q, W.g_q, bf, false, cq, d->d_q_latent, abs + L.off[2], ws, e, s);
+  // column h*R + f of the merged product is element f of head h's row,
+  // rotated from f = d_latent on
+  e.qg_cols = row_width(d); e.qg_stride = row_width(d); e.q_off = 0; e.q_ld = d->n_heads * row_width(d);
+  e.rope_from = d->d_latent;
+  if (!factored(d)) {
+    st = run_gemm(W, G_Q, W.g_q, bf, false, cq, d->d_q_latent, abs + L.off[2], ws, e, s);
+    (void)batch;
+    return st;
+  }
+  // factored: q_nope = c_Q W_UQ (all heads), rounded to dtype
+  const int H = d->n_heads, R = row_width(d);
+  void* qn = ws + W.qn;
+  st = run_gemm(W, G_Q, W.g_qn, bf, false, cq, d->d_q_latent, abs + L.uq, ws, base_epi(EPI_STORE_T, qn), s);
+  if (st) return st;
+  // q_pe[h] = RoPE(c_Q W_QR[h]) into columns d_L.. of head h's row
+  e.qg_cols = d->d_rope; e.qg_stride = R; e.q_off = d->d_latent; e.q_ld = H * R; e.rope_from = 0;
+  st = run_gemm(W, G_Q, W.g_qr, bf, false, cq, d->d_q_latent, abs + L.qr, ws, e, s);
+  if (st) return st;
+  // q_lat[h] = q_nope[h] W_UK[h]^T into columns 0..d_L of head h's row
+  e.qg_cols = d->d_latent; e.qg_stride = R; e.q_off = 0; e.q_ld = H * R; e.rope_from = d->d_latent;
+  st = run_gemm(W, G_Q, W.g_qk, bf, false, qn, H * d->d_nope, abs + L.ukt, ws, e, s);
   (void)batch;
   return st;
 }
@@ -271,6 +346,8 @@ mla_status mla_absorb_weights(const mla_dims* d, const mla_raw_weights* raw, voi
   a.W_DQ = raw->W_DQ; a.W_UQ = raw->W_UQ; a.W_QR = raw->W_QR; a.W_DKV = raw->W_DKV; a.W_KR = raw->W_KR;
   a.W_UK = raw->W_UK; a.W_UV = raw->W_UV; a.W_O = raw->W_O;
   a.P_KV = ab + L.off[0]; a.P_DQ = ab + L.off[1]; a.P_QC = ab + L.off[2]; a.P_O = ab + L.off[3];
+  a.factored = factored(d);
+  a.P_UQ = ab + L.uq; a.P_QR = ab + L.qr; a.P_UKT = ab + L.ukt; a.P_UV = ab + L.uv; a.P_WO = ab + L.wo;
   hipError_t e = launch_absorb(a, is_bf16(d), reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "absorb launch");
   return MLA_OK;
@@ -382,8 +459,16 @@ mla_status mla_out_proj(const mla_dims* d, const void* absorbed, const float* o_
   const bool bf = is_bf16(d);
   const AbsLayout L = abs_layout(d);
   unsigned char* ws = reinterpret_cast<unsigned char*>(workspace);
-  return run_gemm(W, G_OUT, W.g_out, bf, true, o_lat, d->n_heads * d->d_latent,
-                  reinterpret_cast<const unsigned char*>(absorbed) + L.off[3], ws, base_epi(EPI_F32, y), s);
+  const unsigned char* ab = reinterpret_cast<const unsigned char*>(absorbed);
+  if (!factored(d))
+    return run_gemm(W, G_OUT, W.g_out, bf, true, o_lat, d->n_heads * d->d_latent, ab + L.off[3], ws,
+                    base_epi(EPI_F32, y), s);
+  // factored: v[h] = o_lat[h] W_UV[h] (rounded to dtype), then y = v W_O
+  void* vo = ws + W.vo;
+  st = run_gemm(W, G_OUT, W.g_ov, bf, true, o_lat, d->n_heads * d->d_latent, ab + L.uv, ws, base_epi(EPI_STORE_T, vo),
+                s);
+  if (st) return st;
+  return run_gemm(W, G_OUT, W.g_oo, bf, false, vo, d->n_heads * d->d_v, ab + L.wo, ws, base_epi(EPI_F32, y), s);
 }
 
 }  // extern "C"

@@ -37,17 +37,19 @@ __device__ inline void epi_pair(const EpiArgs& e, int m, int n, float v0, float 
     return;
   }
   const int b = m / e.n_q, t = m - b * e.n_q;
-  const int f = n % e.row;  // column within one head's (latent | rope) row
-  const int pos = (e.mode == EPI_Q) ? e.kv_len[b] - e.n_q + t : e.pos[b] + t;
-  if (f >= e.d_latent) {
+  const bool q = e.mode == EPI_Q;
+  // column within its group (EPI_Q) or within one cache row (EPI_APPEND)
+  const int f = n % (q ? e.qg_cols : e.row), rope0 = q ? e.rope_from : e.d_latent;
+  const int pos = q ? e.kv_len[b] - e.n_q + t : e.pos[b] + t;
+  if (f >= rope0) {
     float c, s;
-    rope_cos_sin(pos, (f - e.d_latent) >> 1, e.d_rope, e.rope_base, &c, &s);
+    rope_cos_sin(pos, (f - rope0) >> 1, e.d_rope, e.rope_base, &c, &s);
     const float a0 = v0, a1 = v1;
     v0 = a0 * c - a1 * s;
     v1 = a0 * s + a1 * c;
   }
-  if (e.mode == EPI_Q) {
-    T* y = reinterpret_cast<T*>(e.out) + (size_t)m * e.N + n;
+  if (q) {
+    T* y = reinterpret_cast<T*>(e.out) + (size_t)m * e.q_ld + e.q_off + (size_t)(n / e.qg_cols) * e.qg_stride + f;
     y[0] = from_f32<T>(v0);
     y[1] = from_f32<T>(v1);
     return;
@@ -97,6 +99,7 @@ struct GemmArgs {
   int lda;
   const void* Wp;
   int kblocks, ntiles, Np, ksplit, kb_per_split;
+  int a_gtiles, a_gstride;  // A column groups (0: none)
   float* part;
   EpiArgs e;
 };
@@ -139,11 +142,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
 
   const TA* ap[MT];
   bool aval[MT];
+  // A column group of this wave's tiles (they never straddle two groups)
+  const size_t a_col = g.a_gtiles ? (size_t)(nt0 / g.a_gtiles) * g.a_gstride : 0;
 #pragma unroll
   for (int mi = 0; mi < MT; ++mi) {
     const int m = (mt0 + mi) * 16 + (lane & 15);
     aval[mi] = m < M;
-    ap[mi] = reinterpret_cast<const TA*>(g.A) + (size_t)(aval[mi] ? m : 0) * (size_t)g.lda + (lane >> 4) * KPL;
+    ap[mi] = reinterpret_cast<const TA*>(g.A) + (size_t)(aval[mi] ? m : 0) * (size_t)g.lda + a_col + (lane >> 4) * KPL;
   }
   // k-block-major packed weights: tile nt at k-block kb is fragment kb*ntiles + nt
   const size_t kb_stride = (size_t)g.ntiles * FR;
@@ -337,8 +342,9 @@ __device__ inline void tiled_dma_load(const GemmArgs& g, unsigned char* st, int 
   if (u < aw) {
     // A: rows m0.., k from kb*32; the record count stops at row M (zeros below)
     const long a_rows = live ? (long)max(g.e.M - m0, 0) : 0;
+    const size_t a_col = g.a_gtiles ? (size_t)(nt0 / g.a_gtiles) * g.a_gstride : 0;  // A column group
     const __amdgpu_buffer_rsrc_t ra =
-        gemm_rsrc(reinterpret_cast<const unsigned char*>(g.A) + ((size_t)m0 * g.lda + (size_t)kb * 32) * esa,
+        gemm_rsrc(reinterpret_cast<const unsigned char*>(g.A) + ((size_t)m0 * g.lda + a_col + (size_t)kb * 32) * esa,
                   a_rows * g.lda * esa);
     const int i = wave + 4 * u;
     const int r = i * (1024 / rowb) + lane / cpr, pc = lane % cpr;
@@ -533,14 +539,19 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmArgs g) {
   // column role: latent / rope pair j (rotation frequency in revolutions per position)
   bool rope_col = false;
   double rev_per_pos = 0.0;
+  const bool qm = e.mode == EPI_Q;
   if (rope_mode && n < e.N) {
-    const int f = n % e.row;
-    if (f >= e.d_latent) {
-      const int j = (f - e.d_latent) >> 1;
+    const int f = n % (qm ? e.qg_cols : e.row), rope0 = qm ? e.rope_from : e.d_latent;
+    if (f >= rope0) {
+      const int j = (f - rope0) >> 1;
       rope_col = true;
       rev_per_pos = exp2(-(2.0 * (double)j / (double)e.d_rope) * log2((double)e.rope_base)) * 0.15915494309189535;
     }
   }
+  // bf16 destination of this thread's column pair: row stride and column
+  // offset (EPI_Q maps the column through its groups)
+  const size_t q_ld = qm ? (size_t)e.q_ld : (size_t)e.N;
+  const size_t q_col = (qm && n < e.N) ? (size_t)e.q_off + (size_t)(n / e.qg_cols) * e.qg_stride + n % e.qg_cols : (size_t)n;
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     if (wm == half) {
@@ -622,11 +633,11 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmArgs g) {
             rows([&](int r, float2 v) {
               const int rb = half * HM + r;
               rotate(rb, v);
-              store(reinterpret_cast<__bf16*>(e.out) + (size_t)(m0 + rb) * e.N + n, v.x, v.y);
+              store(reinterpret_cast<__bf16*>(e.out) + (size_t)(m0 + rb) * q_ld + q_col, v.x, v.y);
             });
           } else {
             rows([&](int r, float2 v) {
-              store(reinterpret_cast<__bf16*>(e.out) + (size_t)(m0 + half * HM + r) * e.N + n, v.x, v.y);
+              store(reinterpret_cast<__bf16*>(e.out) + (size_t)(m0 + half * HM + r) * q_ld + q_col, v.x, v.y);
             });
           }
         }
@@ -668,12 +679,16 @@ static int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 // Column-tile counts per wave instantiated for the decode path (16 tiles
 // per wave, one wave per SIMD, measured slower than 10 in every split
-// tried for the output projection).
-static const int kDecodeNT[] = {2, 4, 5, 8, 9, 10};
+// tried for the output projection; 1 only for one-tile A column groups).
+static const int kDecodeNT[] = {1, 2, 4, 5, 8, 9, 10};
 
-GemmPlan plan_gemm(int M, int K, int N, bool bf16, bool a_f32, int n_cu) {
+GemmPlan plan_gemm(int M, int K, int N, bool bf16, bool a_f32, int n_cu, int a_gtiles, int a_gstride) {
   GemmPlan g{};
   g.M = M; g.K = K; g.N = N;
+  g.a_gtiles = a_gtiles; g.a_gstride = a_gstride;
+  // with A column groups, the n-tiles a wave (or tiled block) covers must
+  // lie inside one group
+  auto fits = [&](int tiles) { return a_gtiles == 0 || a_gtiles % tiles == 0; };
   g.KB = bf16 ? Mfma<__bf16>::KB : Mfma<float>::KB;
   g.Kp = ceil_div(K, g.KB) * g.KB;
   g.Np = ceil_div(N, 16) * 16;
@@ -690,6 +705,7 @@ GemmPlan plan_gemm(int M, int K, int N, bool bf16, bool a_f32, int n_cu) {
   double best = 1e300;
   long best_blocks = 0;
   auto consider = [&](int MT, int NT, int KSW) {
+    if (!fits(NT) || (NT == 1 && a_gtiles != 1)) return;  // one-tile waves only for one-tile groups
     const int cols = (4 / KSW) * NT;
     const int gx = ceil_div(g.ntiles, cols), gy = ceil_div(mtiles, MT);
     const int ksmax = std::max(1, g.kblocks / (2 * KSW));
@@ -713,8 +729,9 @@ GemmPlan plan_gemm(int M, int K, int N, bool bf16, bool a_f32, int n_cu) {
     }
   };
   g.tiled = 0;
-  const bool big = M >= 256 && g.ntiles >= 64;  // 256 x 256 tiles, one k-block per stage
-  if (bf16 && M > 16 && (big || g.kblocks % 2 == 0)) {
+  // 256 x 256 tiles (16 n-tiles per block), one k-block per stage
+  const bool big = M >= 256 && g.ntiles >= 64 && fits(16);
+  if (bf16 && M > 16 && (big || g.kblocks % 2 == 0) && fits(8)) {
     // LDS-tiled kernel: 64 x 128 tiles up to 64 rows, 128 x 128 up to 255,
     // 256 x 256 above (one k-block per stage, slices a multiple of a stage)
     g.tiled = 1;
@@ -768,6 +785,7 @@ GemmPlan plan_gemm(int M, int K, int N, bool bf16, bool a_f32, int n_cu) {
   } else {
     consider(4, 4, 1);
   }
+  if (!g.tiled && best == 1e300) g.tiled = -1;  // no configuration fits the A column groups
   g.part_bytes = g.ksplit > 1 ? (size_t)g.ksplit * (size_t)M * (size_t)g.Np * sizeof(float) : 0;
   return g;
 }
@@ -820,6 +838,7 @@ template <typename T, typename TA>
 static hipError_t launch_gemm_sel(const GemmPlan& g, const GemmArgs& a, hipStream_t s) {
   if (g.KSW == 4 && g.MT == 1) {
     switch (g.NT) {
+      case 1: return launch_gemm_t<T, TA, 1, 1, 4>(g, a, s);
       case 2: return launch_gemm_t<T, TA, 1, 2, 4>(g, a, s);
       case 4: return launch_gemm_t<T, TA, 1, 4, 4>(g, a, s);
       case 5: return launch_gemm_t<T, TA, 1, 5, 4>(g, a, s);
@@ -844,6 +863,7 @@ static hipError_t launch_gemm_sel(const GemmPlan& g, const GemmArgs& a, hipStrea
 
 hipError_t launch_gemm(const GemmPlan& g, bool bf16, bool a_f32, const void* A, int lda, const void* Wp, float* part,
                        const EpiArgs& e, hipStream_t s) {
+  if (g.tiled < 0) return hipErrorInvalidConfiguration;
   GemmArgs a{};
   a.A = A;
   a.lda = lda;
@@ -853,6 +873,8 @@ hipError_t launch_gemm(const GemmPlan& g, bool bf16, bool a_f32, const void* A, 
   a.Np = g.Np;
   a.ksplit = g.ksplit;
   a.kb_per_split = g.kb_per_split;
+  a.a_gtiles = g.a_gtiles;
+  a.a_gstride = g.a_gstride;
   a.part = part;
   a.e = e;
   a.e.M = g.M;
@@ -873,10 +895,14 @@ hipError_t launch_gemm(const GemmPlan& g, bool bf16, bool a_f32, const void* A, 
 //   P_QC : K = d_LQ,    N = H * R        per head h: [W_UQ[h] W_UK[h]^T | W_QR[h]]
 //   P_O  : K = H * d_L, N = d_model      row h*d_L + c: (W_UV[h] W_O[h])[c]
 // --------------------------------------------------------------------------
-enum PackMode { PACK_KV = 0, PACK_DQ = 1, PACK_QC = 2, PACK_O = 3 };
+// PACK_PLAIN: element (k, n) of a row-major source with row stride `ld`;
+// PACK_UKT: W_UK[c, h, k] at (k, n = h*d_L + c) (the factored key weight,
+// transposed per head).
+enum PackMode { PACK_KV = 0, PACK_DQ = 1, PACK_QC = 2, PACK_O = 3, PACK_PLAIN = 4, PACK_UKT = 5 };
 
 template <typename T>
-__global__ __launch_bounds__(256) void pack_kernel(AbsorbArgs a, int mode, int K, int N, int Kp, int Np, T* out) {
+__global__ __launch_bounds__(256) void pack_kernel(AbsorbArgs a, int mode, int K, int N, int Kp, int Np, T* out,
+                                                   const T* plain, long ld) {
   using F = Mfma<T>;
   const size_t total = (size_t)Kp * Np;
   const size_t p = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -908,6 +934,14 @@ __global__ __launch_bounds__(256) void pack_kernel(AbsorbArgs a, int mode, int K
         const int h = n / R, f = n % R;
         if (f < a.d_latent) return;  // written by the product kernel
         src = (const T*)a.W_QR; off = ((size_t)k * a.H + h) * a.d_rope + (f - a.d_latent);
+        break;
+      }
+      case PACK_PLAIN:
+        src = plain; off = (size_t)k * ld + n;
+        break;
+      case PACK_UKT: {
+        const int h = n / a.d_latent, c = n % a.d_latent;
+        src = (const T*)a.W_UK; off = ((size_t)c * a.H + h) * a.d_nope + k;
         break;
       }
       default:
@@ -970,6 +1004,34 @@ __global__ __launch_bounds__(256) void absorb_product_kernel(ProdArgs p) {
 }
 
 template <typename T>
+static hipError_t pack_one(const AbsorbArgs& a, int mode, int K, int N, void* out, const void* plain, long ld,
+                           hipStream_t s) {
+  using F = Mfma<T>;
+  const int Kp = ceil_div(K, F::KB) * F::KB, Np = ceil_div(N, 16) * 16;
+  const size_t total = (size_t)Kp * Np;
+  hipLaunchKernelGGL(pack_kernel<T>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a, mode, K, N, Kp, Np,
+                     reinterpret_cast<T*>(out), reinterpret_cast<const T*>(plain), ld);
+  return hipGetLastError();
+}
+
+// Factored form: the raw factors, repacked (no products).
+template <typename T>
+static hipError_t pack_factored_t(const AbsorbArgs& a, hipStream_t s) {
+  const int R = a.d_latent + a.d_rope;
+  hipError_t e;
+  if ((e = pack_one<T>(a, PACK_KV, a.d_model, R, a.P_KV, nullptr, 0, s)) != hipSuccess) return e;
+  if ((e = pack_one<T>(a, PACK_DQ, a.d_model, a.d_q_latent, a.P_DQ, nullptr, 0, s)) != hipSuccess) return e;
+  if ((e = pack_one<T>(a, PACK_PLAIN, a.d_q_latent, a.H * a.d_nope, a.P_UQ, a.W_UQ, (long)a.H * a.d_nope, s)))
+    return e;
+  if ((e = pack_one<T>(a, PACK_PLAIN, a.d_q_latent, a.H * a.d_rope, a.P_QR, a.W_QR, (long)a.H * a.d_rope, s)))
+    return e;
+  if ((e = pack_one<T>(a, PACK_UKT, a.d_nope, a.H * a.d_latent, a.P_UKT, nullptr, 0, s)) != hipSuccess) return e;
+  if ((e = pack_one<T>(a, PACK_PLAIN, a.d_latent, a.H * a.d_v, a.P_UV, a.W_UV, (long)a.H * a.d_v, s)))
+    return e;
+  return pack_one<T>(a, PACK_PLAIN, a.H * a.d_v, a.d_model, a.P_WO, a.W_O, (long)a.d_model, s);
+}
+
+template <typename T>
 static hipError_t absorb_t(const AbsorbArgs& a, hipStream_t s) {
   using F = Mfma<T>;
   const int R = a.d_latent + a.d_rope;
@@ -985,7 +1047,7 @@ static hipError_t absorb_t(const AbsorbArgs& a, hipStream_t s) {
     // PACK_O only has padding to fill; the product kernel writes the rest.
     if (mt.mode == PACK_O && Kp == mt.K && Np == mt.N) continue;
     hipLaunchKernelGGL(pack_kernel<T>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a, mt.mode,
-                       mt.K, mt.N, Kp, Np, reinterpret_cast<T*>(mt.out));
+                       mt.K, mt.N, Kp, Np, reinterpret_cast<T*>(mt.out), nullptr, 0L);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
@@ -1017,6 +1079,7 @@ static hipError_t absorb_t(const AbsorbArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_absorb(const AbsorbArgs& a, bool bf16, hipStream_t s) {
+  if (a.factored) return bf16 ? pack_factored_t<__bf16>(a, s) : pack_factored_t<float>(a, s);
   return bf16 ? absorb_t<__bf16>(a, s) : absorb_t<float>(a, s);
 }
 

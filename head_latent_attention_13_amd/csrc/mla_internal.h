@@ -19,14 +19,21 @@ namespace mla {
 // With ksplit > 1 slices, each block leaves an fp32 partial tile in the
 // workspace and a second kernel sums the slices in order and applies the
 // epilogue.
+// A may be read in column groups: the n-tiles [g*a_gtiles, (g+1)*a_gtiles)
+// take their A operand from columns g*a_gstride .. of A (a per-head product
+// packed as one wide matrix); a block never straddles two groups.
 enum EpiMode { EPI_F32 = 0, EPI_STORE_T = 1, EPI_Q = 2, EPI_APPEND = 3 };
 
 struct EpiArgs {
   int mode;
   int M, N;
-  void* out;            // EPI_F32: float[M][N]; EPI_STORE_T / EPI_Q: T[M][N]
+  void* out;            // EPI_F32: float[M][N]; EPI_STORE_T: T[M][N]; EPI_Q: see below
   // RoPE (EPI_Q, EPI_APPEND)
-  int d_latent, d_rope, row;   // row = d_latent + d_rope
+  int d_latent, d_rope, row;   // row = d_latent + d_rope (EPI_APPEND: the cache row)
+  // EPI_Q: column n is element f = n % qg_cols of group n / qg_cols; it is
+  // stored to out[m * q_ld + q_off + (n / qg_cols) * qg_stride + f] and
+  // rotated (pairs f, f+1 counted from rope_from) when f >= rope_from
+  int qg_cols, qg_stride, q_off, q_ld, rope_from;
   float rope_base;
   int n_q;
   const int32_t* kv_len;       // EPI_Q: query t of sequence b sits at kv_len[b]-n_q+t
@@ -48,10 +55,14 @@ struct GemmPlan {
   int gx, gy;        // blocks over columns / rows
   int ksplit, kb_per_split;
   size_t part_bytes; // fp32 partial tiles (ksplit > 1)
+  int a_gtiles;      // A column groups (0: none): n-tiles per group ...
+  int a_gstride;     // ... and A column offset per group
 };
 
-// a_f32: the A operand is fp32 (converted to bf16 fragments in the kernel)
-GemmPlan plan_gemm(int M, int K, int N, bool bf16, bool a_f32, int n_cu);
+// a_f32: the A operand is fp32 (converted to bf16 fragments in the kernel).
+// a_gtiles / a_gstride: A column groups (0: none).  Returns a plan with
+// tiled == -1 when no kernel configuration fits the groups.
+GemmPlan plan_gemm(int M, int K, int N, bool bf16, bool a_f32, int n_cu, int a_gtiles = 0, int a_gstride = 0);
 
 // A is T (a_f32 == false) or fp32 (a_f32 == true); Wp is T.
 hipError_t launch_gemm(const GemmPlan& g, bool bf16, bool a_f32, const void* A, int lda, const void* Wp, float* part,
@@ -61,7 +72,9 @@ hipError_t launch_gemm(const GemmPlan& g, bool bf16, bool a_f32, const void* A, 
 struct AbsorbArgs {
   int d_model, H, d_latent, d_q_latent, d_nope, d_rope, d_v;
   const void *W_DQ, *W_UQ, *W_QR, *W_DKV, *W_KR, *W_UK, *W_UV, *W_O;
-  void *P_KV, *P_DQ, *P_QC, *P_O;   // packed outputs
+  void *P_KV, *P_DQ, *P_QC, *P_O;   // packed outputs (merged form: all four)
+  int factored;                      // factored form: P_KV, P_DQ and these five
+  void *P_UQ, *P_QR, *P_UKT, *P_UV, *P_WO;
 };
 hipError_t launch_absorb(const AbsorbArgs& a, bool bf16, hipStream_t s);
 

@@ -69,6 +69,22 @@ typedef enum mla_status {
 
 typedef enum mla_dtype { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
 
+/* How the absorbed weights are held (mla_dims.weight_form).
+ *   MLA_WEIGHTS_MERGED: the two merges are precomputed, W_UQ[h] W_UK[h]^T
+ *     (d_LQ x d_L per head) and W_UV[h] W_O[h] (d_L x d_model per head)
+ *     (page "Multi-Head Latent Attention (MLA)", "Two merges are where the
+ *     compute win comes from").
+ *   MLA_WEIGHTS_FACTORED: the same products taken in two steps at run time,
+ *     q_lat[h] = (c_Q W_UQ[h]) W_UK[h]^T and y = sum_h (o_lat[h] W_UV[h]) W_O[h]
+ *     (page "Multi-Head Latent Attention (MLA)", "The construction": the
+ *     factors themselves; per-head keys and values are still never formed).
+ *     Fewer weight bytes per step when d_nope, d_v < d_L (the DeepSeek-V2
+ *     shapes: 0.30 GB instead of 0.92 GB); the intermediate c_Q W_UQ[h] and
+ *     o_lat[h] W_UV[h] are rounded to dtype.
+ * Every entry point that takes `absorbed` follows dims->weight_form; the
+ * attention itself (mla_attention) does not depend on it. */
+typedef enum mla_weight_form { MLA_WEIGHTS_MERGED = 0, MLA_WEIGHTS_FACTORED = 1 } mla_weight_form;
+
 /* Model dimensions of one MLA layer. */
 typedef struct mla_dims {
   int32_t d_model;     /* token hidden width */
@@ -81,6 +97,7 @@ typedef struct mla_dims {
   int32_t dtype;       /* mla_dtype */
   float rope_base;     /* RoPE frequency base, e.g. 10000 */
   float softmax_scale; /* 0 => 1/sqrt(d_nope + d_rope) */
+  int32_t weight_form; /* mla_weight_form (0 = merged) */
 } mla_dims;
 
 /* Raw (unmerged) weights, device, dtype, row-major with these shapes:
@@ -116,8 +133,9 @@ const char *mla_last_error(void);
 const char *mla_version(void);
 
 /* Layout of the absorbed-weight buffer (host only, no device work).
- * The buffer holds four matrices in the packed fragment order described
+ * The buffer holds four regions in the packed fragment order described
  * below, at byte offsets[i] with sizes bytes[i]; *total is the buffer size.
+ * Merged form (one matrix per region):
  *   [0] W_DKVR : K = d_model,  N = R          [W_DKV | W_KR]
  *   [1] W_DQ   : K = d_model,  N = d_LQ
  *   [2] W_QC   : K = d_LQ,     N = H * R      column h*R + f:
@@ -127,6 +145,13 @@ const char *mla_version(void);
  *                f >= d_L : W_QR[:, h, f - d_L]
  *   [3] W_UVO  : K = H * d_L,  N = d_model    row h*d_L + c:
  *                (W_UV[h] W_O[h])[c, :]  (merged, output side)
+ * Factored form: [0] and [1] as above; region [2] holds three matrices and
+ * region [3] two, each starting at a 256-byte boundary in this order:
+ *   [2] W_UQ  : K = d_LQ,   N = H * d_nope   column h*d_nope + f: W_UQ[:, h, f]
+ *       W_QR  : K = d_LQ,   N = H * d_rope   column h*d_rope + f: W_QR[:, h, f]
+ *       W_UKT : K = d_nope, N = H * d_L      column h*d_L + c:    W_UK[c, h, :]
+ *   [3] W_UV  : K = d_L,    N = H * d_v      column h*d_v + f:    W_UV[:, h, f]
+ *       W_O   : K = H*d_v,  N = d_model      row h*d_v + f:       W_O[h, f, :]
  * Packed order of a logical K x N matrix W (y = x W): element (k, n) sits at
  *   ((k/KB) * (Np/16) + n/16) * 64*KPL + ((n%16) + 16*((k%KB)/KPL)) * KPL + k%KPL
  * with KB = 32, KPL = 8 for bf16 (KB = 4, KPL = 1 for fp32), Np = N rounded
@@ -137,7 +162,8 @@ const char *mla_version(void);
 mla_status mla_absorbed_layout(const mla_dims *dims, size_t offsets[4], size_t bytes[4], size_t *total);
 
 /* One-time weight absorption: fills `absorbed` (size from
- * mla_absorbed_layout) from the raw weights.  Products accumulate in fp32
+ * mla_absorbed_layout, in dims->weight_form) from the raw weights (the
+ * factored form only repacks them).  Products accumulate in fp32
  * and are rounded once to dtype.  Raw weights are only read. */
 mla_status mla_absorb_weights(const mla_dims *dims, const mla_raw_weights *raw, void *absorbed,
                               size_t absorbed_bytes, void *stream);
@@ -168,7 +194,8 @@ mla_status mla_compress_append(const mla_dims *dims, const void *absorbed, const
                                size_t ws_bytes, void *stream);
 
 /* Query projection with the merged query weight (page "Multi-Head Latent
- * Attention (MLA)", "Two merges", query side; "The RoPE problem").
+ * Attention (MLA)", "Two merges", query side; "The RoPE problem"), or in the
+ * factored form c_Q W_UQ[h] (rounded to dtype) times W_UK[h]^T.
  *   x [batch * n_q, d_model] dtype; kv_len [batch] int32 (the n_q new tokens
  *   of sequence b sit at positions kv_len[b]-n_q .. kv_len[b]-1)
  *   q [batch * n_q, H, R] dtype out: [c_Q W_UQK[h] | RoPE(c_Q W_QR[h])] */
@@ -195,7 +222,9 @@ mla_status mla_decode(const mla_dims *dims, const void *absorbed, const void *x,
                       void *workspace, size_t ws_bytes, void *stream);
 
 /* Absorbed output projection (page "Multi-Head Latent Attention (MLA)",
- * "Two merges", output side): y[n] = sum_h o_lat[n][h] W_UVO[h].
+ * "Two merges", output side): y[n] = sum_h o_lat[n][h] W_UVO[h]; in the
+ * factored form v[h] = o_lat[n][h] W_UV[h] (rounded to dtype), then
+ * y[n] = sum_h v[h] W_O[h].
  *   o_lat [n_tok, H, d_latent] fp32;  y [n_tok, d_model] fp32 out. */
 mla_status mla_out_proj(const mla_dims *dims, const void *absorbed, const float *o_lat, int32_t n_tok, float *y,
                         void *workspace, size_t ws_bytes, void *stream);

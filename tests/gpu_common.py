@@ -15,9 +15,9 @@ BF16_REL_L2, BF16_MAX_ABS = 1e-2, 3e-2
 F32_REL_L2, F32_MAX_ABS = 1e-5, 1e-5
 
 
-def dims_of(cfg):
+def dims_of(cfg, form="merged"):
     return mla.make_dims(cfg.d_model, cfg.n_heads, cfg.d_latent, cfg.d_q_latent, cfg.d_nope, cfg.d_rope, cfg.d_v,
-                         cfg.dtype, cfg.rope_base)
+                         cfg.dtype, cfg.rope_base, form=form)
 
 
 def tdtype(cfg):
