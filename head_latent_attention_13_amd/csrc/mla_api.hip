@@ -102,29 +102,36 @@ size_t packed_bytes(const mla_dims* d, int K, int N) {
 AbsLayout abs_layout(const mla_dims* d) {
   const int R = row_width(d), H = d->n_heads;
   AbsLayout L{};
-  size_t o = 0;
+  size_t o = 0, end = 0;  // next free 256-byte boundary, end of the last matrix
   auto put = [&](int K, int N) {
     const size_t at = o;
-    o = align256(o + packed_bytes(d, K, N));
+    end = o + packed_bytes(d, K, N);
+    o = align256(end);
     return at;
   };
+  size_t ends[4];
   L.off[0] = put(d->d_model, R);
+  ends[0] = end;
   L.off[1] = put(d->d_model, d->d_q_latent);
+  ends[1] = end;
   L.off[2] = o;
   if (!factored(d)) {
     put(d->d_q_latent, H * R);
+    ends[2] = end;
     L.off[3] = o;
     put(H * d->d_latent, d->d_model);
   } else {
     L.uq = put(d->d_q_latent, H * d->d_nope);
     L.qr = put(d->d_q_latent, H * d->d_rope);
     L.ukt = put(d->d_nope, H * d->d_latent);
+    ends[2] = end;
     L.off[3] = o;
     L.uv = put(d->d_latent, H * d->d_v);
     L.wo = put(H * d->d_v, d->d_model);
   }
+  ends[3] = end;
   L.total = o;
-  for (int i = 0; i < 4; ++i) L.bytes[i] = (i < 3 ? L.off[i + 1] : L.total) - L.off[i];
+  for (int i = 0; i < 4; ++i) L.bytes[i] = ends[i] - L.off[i];  // region i: its matrices and the gaps between them
   return L;
 }
 

@@ -69,6 +69,42 @@ def test_absorbed_layout_pads_fp32_tiny():
     assert sizes[2] == 48 * 160 * 4
 
 
+def test_factored_layout_holds_the_repacked_factors():
+    """Factored form: region 2 = W_UQ | W_QR | W_UK^T, region 3 = W_UV | W_O,
+    each matrix at a 256-byte boundary; about a third of the merged bytes
+    at the DeepSeek-V2 shapes."""
+    _lib()
+    d = mla.make_dims(5120, 128, 512, 1536, 128, 64, 128, "bf16", form="factored")
+    offs, sizes, total = mla.mla_absorbed_layout(d)
+    R, H, e = 576, 128, 2
+    al = lambda x: -(-x // 256) * 256
+    uq, qr, ukt = 1536 * H * 128 * e, 1536 * H * 64 * e, 128 * H * 512 * e
+    uv, wo = 512 * H * 128 * e, H * 128 * 5120 * e
+    assert sizes[:2] == [5120 * R * e, 5120 * 1536 * e]
+    assert sizes[2] == al(uq) + al(qr) + ukt and sizes[3] == al(uv) + wo
+    assert offs[3] == offs[2] + al(sizes[2]) and total == offs[3] + al(sizes[3])
+    _, msizes, mtotal = mla.mla_absorbed_layout(v2_dims())
+    assert total < 0.35 * mtotal
+    # tiny fp32 shape: padded columns (N = 4 * 8 = 32 needs none; K = 16 none)
+    t = mla.make_dims(64, 4, 32, 48, 16, 8, 16, "f32", form="factored")
+    offs, sizes, total = mla.mla_absorbed_layout(t)
+    assert sizes[3] == al(32 * 64 * 4) + 64 * 64 * 4
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("weight_form", 2, -1),   # not a form
+    ("d_v", 120, -2),         # per-head value width not whole 16-column tiles
+    ("d_nope", 112, -2),      # run-time reduction width not a multiple of 32 (bf16)
+])
+def test_factored_dims_checked(field, value, code):
+    _lib()
+    d = mla.make_dims(5120, 128, 512, 1536, 128, 64, 128, "bf16", form="factored")
+    setattr(d, field, value)
+    with pytest.raises(mla.MLAError) as e:
+        mla.mla_workspace_size(d, 16, 1)
+    assert e.value.status == code
+
+
 def test_workspace_size_grows_with_batch():
     _lib()
     d = v2_dims()
