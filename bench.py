@@ -28,6 +28,7 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 F32_PEAK_TFLOPS = 157.3      # MI355X dense fp32 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+MFMA_FILE = os.path.join(ROOT, "profiles", "mfma.txt")
 KERNEL_SOURCES = ("mla_gemm.hip", "mla_attn.hip", "mla_common.h")
 
 
@@ -46,6 +47,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget for the oracle sample")
     p.add_argument("--copy-calib-mb", type=int, default=0,
                    help="only run a plain device copy of this many MB (counter calibration)")
+    p.add_argument("--mfma-calib", type=int, default=0,
+                   help="only run a bf16 n x n x n matrix product (MFMA counter calibration)")
     return p.parse_args()
 
 
@@ -70,6 +73,20 @@ def measured_traffic(call: str, workload: str):
     return t.get("calls", {}).get(call)
 
 
+def measured_mfma(workload: str):
+    """MFMA counters per call (counted GFLOP, busy % of SIMD cycles) from the
+    committed counter run, if it was taken on this workload with the current
+    kernel sources; else None."""
+    try:
+        with open(MFMA_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != kernel_source_hash() or t.get("workload") != workload:
+        return None
+    return t.get("calls")
+
+
 def copy_calibration(mb: int, steps: int):
     """A plain streaming kernel of known traffic (reads and writes mb MiB per
     launch) for scaling the HBM byte counters."""
@@ -81,6 +98,18 @@ def copy_calibration(mb: int, steps: int):
         torch.add(a, 1.0, out=b)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4, "launches": steps}))
+
+
+def mfma_calibration(n: int, steps: int):
+    """A bf16 matrix product of known flop count (2 n^3 per launch) for
+    scaling the MFMA operation counter."""
+    import torch
+    a = torch.ones(n, n, dtype=torch.bfloat16, device="cuda")
+    b = torch.ones(n, n, dtype=torch.bfloat16, device="cuda")
+    for _ in range(steps):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    print(json.dumps({"mfma_calibration_flops": 2 * n ** 3, "launches": steps}))
 
 
 def cpu_baseline(case, n_budget_s: float):
@@ -149,6 +178,9 @@ def main():
 
     if args.copy_calib_mb:
         copy_calibration(args.copy_calib_mb, args.steps)
+        return
+    if args.mfma_calib:
+        mfma_calibration(args.mfma_calib, args.steps)
         return
 
     import head_latent_attention_13_amd as mla
@@ -329,6 +361,9 @@ def main():
         # measured from the allocation (paged pools round up to whole pages)
         "kv_bytes_per_token_per_layer": round(pool.numel() * pool.element_size() / int(kv_len.sum()), 1),
         "kernels": kernels,
+        # rocprofv3 counters (SQ_INSTS_VALU_MFMA_MOPS_BF16 calibrated on a product of known size,
+        # SQ_VALU_MFMA_BUSY_CYCLES / GRBM_GUI_ACTIVE), when taken on these kernel sources
+        "mfma_counters": (measured_mfma(cfg.name) if args.form == "merged" else None),
         "absorb_ms_once": round(absorb_ms, 3),
     }
     if not args.no_cpu_baseline:

@@ -7,11 +7,16 @@ Runs, each as its own rocprofv3 process with the program directly after
   1. ``--kernel-trace --stats`` over a short bench run (per-kernel durations);
   2. ``--pmc FETCH_SIZE`` and 3. ``--pmc WRITE_SIZE`` over a 3-step bench run;
   4./5. the same two counters over a plain device copy of known size
-     (``bench.py --copy-calib-mb``), which calibrates the counters to bytes.
+     (``bench.py --copy-calib-mb``), which calibrates the counters to bytes;
+  6. ``--pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES
+     GRBM_GUI_ACTIVE`` over a 3-step bench run and 7. over a bf16 matrix
+     product of known flop count (``bench.py --mfma-calib``): MFMA flops per
+     call and the fraction of SIMD cycles the matrix units were busy.
 
-Writes profiles/kernel_stats_<workload>.txt, profiles/hbm_traffic_<workload>.txt
-and, for the default workload, profiles/hbm_traffic.txt (JSON read by
-bench.py: HBM bytes per call, tagged with a hash of the kernel sources).
+Writes profiles/kernel_stats_<workload>.txt, profiles/hbm_traffic_<workload>.txt,
+profiles/mfma_<workload>.txt and, for the default workload,
+profiles/hbm_traffic.txt and profiles/mfma.txt (JSON read by bench.py: HBM
+bytes and MFMA counters per call, tagged with a hash of the kernel sources).
 
     python bench_counters.py [--config 1] [--out gpurun_out/counters]
 """
@@ -28,6 +33,10 @@ import sys
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CALLS = ("mla_compress_append", "mla_q_proj", "mla_attention", "mla_out_proj")
 COPY_MB = 512
+MFMA_N = 4096
+MFMA_CTRS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+N_SIMD = 1024  # 256 CUs x 4 SIMDs
+N_XCD = 8      # GRBM_GUI_ACTIVE comes summed over the XCDs' graphics blocks
 
 
 def run(cmd, out_dir, name, timeout):
@@ -67,6 +76,17 @@ def counter_per_dispatch(path):
             name, val = r["Kernel_Name"], float(r["Counter_Value"])
             prev = out.get(d, (name, 0.0))
             out[d] = (name, prev[1] + val)
+    return out
+
+
+def counters_per_dispatch(path):
+    """{dispatch id: (kernel name, {counter name: summed value})}"""
+    out = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            d = int(r["Dispatch_Id"])
+            name, vals = out.setdefault(d, (r["Kernel_Name"], {}))
+            vals[r["Counter_Name"]] = vals.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
     return out
 
 
@@ -134,6 +154,21 @@ def main():
             run(cmd, args.out, "copy_" + ctr, 120)
         pmc["copy_" + ctr] = counter_per_dispatch(find(args.out, "copy_" + ctr, "counter_collection.csv"))
 
+    # MFMA counters over the bench and over a matrix product of known size
+    mf_cmd = ["timeout", "-s", "KILL", "120", "rocprofv3", "--pmc", *MFMA_CTRS, "--output-format", "csv", "-d",
+              os.path.join(args.out, "pmc_mfma"), "-o", "run", "--"] + bench + ["--steps", "3", "--warmup", "1"]
+    cal_cmd = ["timeout", "-s", "KILL", "60", "rocprofv3", "--pmc", *MFMA_CTRS, "--output-format", "csv", "-d",
+               os.path.join(args.out, "cal_mfma"), "-o", "run", "--", py, os.path.join(ROOT, "bench.py"),
+               "--mfma-calib", str(MFMA_N), "--steps", "3"]
+    if not args.summarize_only:
+        run(mf_cmd, args.out, "pmc_mfma", 180)
+        run(cal_cmd, args.out, "cal_mfma", 120)
+    mf = counters_per_dispatch(find(args.out, "pmc_mfma", "counter_collection.csv"))
+    cal = counters_per_dispatch(find(args.out, "cal_mfma", "counter_collection.csv"))
+    cal_mops = sorted(v["SQ_INSTS_VALU_MFMA_MOPS_BF16"] for n, v in cal.values()
+                      if v.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0) > 0)
+    flops_per_mop = 2.0 * MFMA_N ** 3 / cal_mops[len(cal_mops) // 2]
+
     # calibration: the copy reads and writes COPY_MB MiB per launch
     true_bytes = COPY_MB * (1 << 20)
     factors = {}
@@ -154,6 +189,23 @@ def main():
     stats = find(args.out, "trace", "kernel_stats.csv")
     with open(stats) as f:
         krows = sorted(csv.DictReader(f), key=lambda r: -float(r["TotalDurationNs"]))
+    avg_us = {r["Name"]: float(r["AverageNs"]) / 1e3 for r in krows}
+
+    # MFMA per dispatch of the last step: counted flops, busy fraction, and
+    # the rate over the kernel's average duration in the trace pass
+    mrows, mcalls = [], {c: {"flops": 0.0, "us": 0.0, "busy": 0.0, "active": 0.0} for c in CALLS}
+    mf_step = last_step({d: (n, d) for d, (n, _) in mf.items()})
+    for call, name, d in mf_step:
+        v = mf[int(d)][1]
+        flops = v.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * flops_per_mop
+        busy, active = v.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0), v.get("GRBM_GUI_ACTIVE", 0.0) / N_XCD
+        us = avg_us.get(name, float("nan"))
+        mrows.append((call, name, flops, busy / (active * N_SIMD) if active else 0.0, us))
+        m = mcalls[call]
+        m["flops"] += flops
+        m["us"] += us
+        m["busy"] += busy
+        m["active"] += active * N_SIMD
     sys.path.insert(0, ROOT)
     from synthetic import config
     workload = config(args.config).name
@@ -179,8 +231,31 @@ def main():
             f.write(f"{call:22s} {name[:70]:70s} {fk:12.0f} {wk:12.0f} {fb / 1e6:10.2f} {wb / 1e6:10.2f}\n")
         for c in CALLS:
             f.write(f"# {c}: {calls[c] / 1e6:.2f} MB per call (read + write)\n")
+    with open(os.path.join(prof, f"mfma_{workload}.txt"), "w") as f:
+        f.write(f"# MFMA counters per dispatch, workload {workload}, last step of a 3-step bench run\n")
+        f.write("# command: " + " ".join(mf_cmd).replace(ROOT, ".").replace(args.out, "<dir>") + "\n")
+        f.write("# calibration: " + " ".join(cal_cmd).replace(ROOT, ".").replace(args.out, "<dir>") +
+                f" ; {flops_per_mop:.1f} flops per counted operation (2 n^3 over the product's counter)\n")
+        f.write(f"# busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {N_XCD} XCDs x {N_SIMD} SIMDs); "
+                f"rate = counted flops / "
+                f"the kernel's average duration in the kernel-trace run; peak 2500 TFLOP/s (dense bf16)\n")
+        f.write(f"{'call':22s} {'kernel':70s} {'GFLOP':>10s} {'avg_us':>9s} {'TFLOP/s':>9s} {'%peak':>7s} {'busy%':>7s}\n")
+        for call, name, fl, bz, us in mrows:
+            f.write(f"{call:22s} {name[:70]:70s} {fl / 1e9:10.3f} {us:9.2f} {fl / (us * 1e-6) / 1e12:9.1f} "
+                    f"{100 * fl / (us * 1e-6) / 2.5e15:7.2f} {100 * bz:7.2f}\n")
+        for c in CALLS:
+            m = mcalls[c]
+            f.write(f"# {c}: {m['flops'] / 1e9:.3f} GFLOP counted, {m['flops'] / (m['us'] * 1e-6) / 1e12:.1f} TFLOP/s "
+                    f"({100 * m['flops'] / (m['us'] * 1e-6) / 2.5e15:.2f}% of peak), MFMA busy "
+                    f"{100 * m['busy'] / max(m['active'], 1):.2f}% of SIMD cycles\n")
     if args.config == 1:
         import bench
+        mout = {"workload": workload, "source_hash": bench.kernel_source_hash(), "flops_per_mop": flops_per_mop,
+                "calls": {c: {"gflop": round(m["flops"] / 1e9, 4),
+                              "busy_pct": round(100 * m["busy"] / max(m["active"], 1), 2)} for c, m in mcalls.items()}}
+        with open(os.path.join(prof, "mfma.txt"), "w") as f:
+            json.dump(mout, f, indent=1)
+            f.write("\n")
         out = {"workload": workload, "source_hash": bench.kernel_source_hash(), "factors": factors,
                "calls": {c: round(v) for c, v in calls.items()}}
         with open(os.path.join(prof, "hbm_traffic.txt"), "w") as f:
