@@ -76,6 +76,12 @@ _SIGS = {
                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "mla_out_proj": (ctypes.c_int32, [ctypes.POINTER(mla_dims), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "mla_prefill_workspace_size": (ctypes.c_int32, [ctypes.POINTER(mla_dims), ctypes.c_int32, ctypes.c_int32,
+                                                    ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]),
+    "mla_prefill_expanded": (ctypes.c_int32, [ctypes.POINTER(mla_dims), ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                              ctypes.POINTER(mla_cache), ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
 }
 
 EXPORTED = tuple(_SIGS)
@@ -194,6 +200,20 @@ def mla_decode(dims, absorbed, x, kv_len, batch, n_q, cache: Cache, o_lat, lse, 
     _check("mla_decode", load().mla_decode(ctypes.byref(dims), _ptr(absorbed), _ptr(x), _ptr(kv_len), batch, n_q,
                                            ctypes.byref(cc), _ptr(o_lat), _ptr(lse), _ptr(workspace),
                                            _nbytes(workspace), _stream(stream)))
+
+
+def mla_prefill_workspace_size(dims: mla_dims, batch: int, n_q: int, s_max: int) -> int:
+    n = ctypes.c_size_t()
+    _check("mla_prefill_workspace_size",
+           load().mla_prefill_workspace_size(ctypes.byref(dims), batch, n_q, s_max, ctypes.byref(n)))
+    return n.value
+
+
+def mla_prefill_expanded(dims, absorbed, x, kv_len, batch, n_q, cache: Cache, y, lse, workspace, stream=None):
+    cc = cache.c()
+    _check("mla_prefill_expanded", load().mla_prefill_expanded(
+        ctypes.byref(dims), _ptr(absorbed), _ptr(x), _ptr(kv_len), batch, n_q, ctypes.byref(cc), _ptr(y), _ptr(lse),
+        _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
 def mla_out_proj(dims, absorbed, o_lat, n_tok, y, workspace, stream=None):

@@ -90,8 +90,8 @@ float scale_of(const mla_dims* d) {
 // ---------------------------------------------------------- absorbed ----
 struct AbsLayout {
   size_t off[4], bytes[4], total;
-  // factored form: byte offsets of W_UQ, W_QR, W_UKT (region 2), W_UV, W_O (region 3)
-  size_t uq, qr, ukt, uv, wo;
+  // factored form: byte offsets of W_UQ, W_QR, W_UKT, W_UK (region 2), W_UV, W_O (region 3)
+  size_t uq, qr, ukt, uk, uv, wo;
 };
 
 size_t packed_bytes(const mla_dims* d, int K, int N) {
@@ -124,6 +124,7 @@ AbsLayout abs_layout(const mla_dims* d) {
     L.uq = put(d->d_q_latent, H * d->d_nope);
     L.qr = put(d->d_q_latent, H * d->d_rope);
     L.ukt = put(d->d_nope, H * d->d_latent);
+    L.uk = put(d->d_latent, H * d->d_nope);
     ends[2] = end;
     L.off[3] = o;
     L.uv = put(d->d_latent, H * d->d_v);
@@ -304,6 +305,48 @@ mla_status check_common(const mla_dims* d, const void* absorbed, int batch, int 
   return MLA_OK;
 }
 
+// ----------------------------------------------------- expanded prefill ----
+struct PfLayout {
+  size_t err, cq, qe, ke, ve, vo, part, total;
+  GemmPlan g_cq, g_qn, g_qr, g_k, g_v, g_oo;
+  bool plans_ok;
+};
+
+PfLayout pf_layout(const mla_dims* d, int batch, int n_q, int s_max) {
+  PfLayout P{};
+  const int M = batch * n_q, Mk = batch * s_max, H = d->n_heads, ncu = device_cus();
+  const int QE = d->d_nope + d->d_rope;
+  P.g_cq = plan_gemm(M, d->d_model, d->d_q_latent, true, false, ncu);
+  P.g_qn = plan_gemm(M, d->d_q_latent, H * d->d_nope, true, false, ncu);
+  P.g_qr = plan_gemm(M, d->d_q_latent, H * d->d_rope, true, false, ncu);
+  P.g_k = plan_gemm(Mk, d->d_latent, H * d->d_nope, true, false, ncu);
+  P.g_v = plan_gemm(Mk, d->d_latent, H * d->d_v, true, false, ncu);
+  P.g_oo = plan_gemm(M, H * d->d_v, d->d_model, true, false, ncu);
+  size_t part = 0;
+  for (const GemmPlan* g : {&P.g_cq, &P.g_qn, &P.g_qr, &P.g_k, &P.g_v, &P.g_oo}) part = std::max(part, g->part_bytes);
+  P.plans_ok = true;
+  size_t o = 0;
+  P.err = o; o = align256(o + 256);
+  P.cq = o; o = align256(o + (size_t)M * d->d_q_latent * 2);
+  P.qe = o; o = align256(o + (size_t)M * H * QE * 2);
+  P.ke = o; o = align256(o + (size_t)Mk * H * d->d_nope * 2);
+  P.ve = o; o = align256(o + (size_t)Mk * H * d->d_v * 2);
+  P.vo = o; o = align256(o + (size_t)M * H * d->d_v * 2);
+  P.part = o; o = align256(o + part);
+  P.total = o;
+  return P;
+}
+
+mla_status check_prefill(const mla_dims* d, int batch, int n_q, int s_max) {
+  mla_status st = check_common(d, nullptr, batch, n_q);
+  if (st) return st;
+  if (!factored(d)) return fail(MLA_ERR_UNSUPPORTED, "expanded prefill needs the factored weight form");
+  if (!prefill_supported(is_bf16(d), d->d_nope, d->d_rope, d->d_v))
+    return fail(MLA_ERR_UNSUPPORTED, "expanded prefill is built for bf16, d_nope = d_v = 128, d_rope = 64");
+  if (s_max <= 0 || (long)batch * s_max > (1L << 26)) return fail(MLA_ERR_INVALID_ARG, "s_max %d", s_max);
+  return MLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -354,7 +397,8 @@ mla_status mla_absorb_weights(const mla_dims* d, const mla_raw_weights* raw, voi
   a.W_UK = raw->W_UK; a.W_UV = raw->W_UV; a.W_O = raw->W_O;
   a.P_KV = ab + L.off[0]; a.P_DQ = ab + L.off[1]; a.P_QC = ab + L.off[2]; a.P_O = ab + L.off[3];
   a.factored = factored(d);
-  a.P_UQ = ab + L.uq; a.P_QR = ab + L.qr; a.P_UKT = ab + L.ukt; a.P_UV = ab + L.uv; a.P_WO = ab + L.wo;
+  a.P_UQ = ab + L.uq; a.P_QR = ab + L.qr; a.P_UKT = ab + L.ukt; a.P_UK = ab + L.uk; a.P_UV = ab + L.uv;
+  a.P_WO = ab + L.wo;
   hipError_t e = launch_absorb(a, is_bf16(d), reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "absorb launch");
   return MLA_OK;
@@ -476,6 +520,65 @@ mla_status mla_out_proj(const mla_dims* d, const void* absorbed, const float* o_
                 s);
   if (st) return st;
   return run_gemm(W, G_OUT, W.g_oo, bf, false, vo, d->n_heads * d->d_v, ab + L.wo, ws, base_epi(EPI_F32, y), s);
+}
+
+mla_status mla_prefill_workspace_size(const mla_dims* d, int32_t batch, int32_t n_q, int32_t s_max, size_t* bytes) {
+  mla_status st = check_prefill(d, batch, n_q, s_max);
+  if (st) return st;
+  if (!bytes) return fail(MLA_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = pf_layout(d, batch, n_q, s_max).total;
+  return MLA_OK;
+}
+
+mla_status mla_prefill_expanded(const mla_dims* d, const void* absorbed, const void* x, const int32_t* kv_len,
+                                int32_t batch, int32_t n_q, const mla_cache* cache, float* y, float* lse,
+                                void* workspace, size_t ws_bytes, void* stream) {
+  if (!cache) return fail(MLA_ERR_INVALID_ARG, "cache is NULL");
+  mla_status st = check_prefill(d, batch, n_q, cache->s_max);
+  if (st) return st;
+  if (absorbed && !aligned(absorbed, 256)) return fail(MLA_ERR_INVALID_ARG, "absorbed buffer must be 256-byte aligned");
+  if (!absorbed || !x || !kv_len || !y) return fail(MLA_ERR_INVALID_ARG, "absorbed, x, kv_len and y must be non-NULL");
+  if (!aligned(x, 16) || !aligned(y, 16)) return fail(MLA_ERR_INVALID_ARG, "x and y must be 16-byte aligned");
+  if ((st = check_cache(d, cache, batch))) return st;
+  if (cache->page_table) return fail(MLA_ERR_UNSUPPORTED, "expanded prefill reads a contiguous cache");
+  const PfLayout P = pf_layout(d, batch, n_q, cache->s_max);
+  if (!workspace || !aligned(workspace, 256)) return fail(MLA_ERR_INVALID_ARG, "workspace must be non-NULL and 256-byte aligned");
+  if (ws_bytes < P.total) return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, P.total);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  unsigned char* ws = reinterpret_cast<unsigned char*>(workspace);
+  const unsigned char* ab = reinterpret_cast<const unsigned char*>(absorbed);
+  const AbsLayout L = abs_layout(d);
+  const int H = d->n_heads, R = row_width(d), QE = d->d_nope + d->d_rope;
+  float* part = reinterpret_cast<float*>(ws + P.part);
+  auto gemm = [&](const GemmPlan& g, bool a_f32, const void* A, int lda, const unsigned char* Wp, const EpiArgs& e) {
+    hipError_t err = launch_gemm(g, true, a_f32, A, lda, Wp, part, e, s);
+    return err == hipSuccess ? MLA_OK : hip_fail(err, "gemm launch");
+  };
+  // queries: c_Q, then [q_nope | RoPE(q_pe)] per head (192 wide)
+  void* cq = ws + P.cq;
+  void* qe = ws + P.qe;
+  if ((st = gemm(P.g_cq, false, x, d->d_model, ab + L.off[1], base_epi(EPI_STORE_T, cq)))) return st;
+  EpiArgs e = base_epi(EPI_Q, qe);
+  e.d_latent = d->d_latent; e.d_rope = d->d_rope; e.row = R; e.rope_base = d->rope_base;
+  e.n_q = n_q; e.kv_len = kv_len;
+  e.qg_cols = d->d_nope; e.qg_stride = QE; e.q_off = 0; e.q_ld = H * QE; e.rope_from = d->d_nope;
+  if ((st = gemm(P.g_qn, false, cq, d->d_q_latent, ab + L.uq, e))) return st;
+  e.qg_cols = d->d_rope; e.qg_stride = QE; e.q_off = d->d_nope; e.q_ld = H * QE; e.rope_from = 0;
+  if ((st = gemm(P.g_qr, false, cq, d->d_q_latent, ab + L.qr, e))) return st;
+  // per-head keys and values of every cache slot: c W_UK[h], c W_UV[h]
+  void* ke = ws + P.ke;
+  void* ve = ws + P.ve;
+  if ((st = gemm(P.g_k, false, cache->pool, R, ab + L.uk, base_epi(EPI_STORE_T, ke)))) return st;
+  if ((st = gemm(P.g_v, false, cache->pool, R, ab + L.uv, base_epi(EPI_STORE_T, ve)))) return st;
+  // causal attention per head, then y = sum_h v[h] W_O[h]
+  PrefillArgs a{};
+  a.qe = qe; a.ke = ke; a.ve = ve; a.pool = cache->pool; a.kv_len = kv_len;
+  a.B = batch; a.n_q = n_q; a.H = H; a.s_max = cache->s_max;
+  a.scale_log2 = scale_of(d) * 1.4426950408889634f;
+  a.vo = ws + P.vo; a.lse = lse; a.err = reinterpret_cast<int32_t*>(ws + P.err);
+  hipError_t err = launch_prefill_attention(a, s);
+  if (err != hipSuccess) return hip_fail(err, "prefill attention launch");
+  return gemm(P.g_oo, false, ws + P.vo, H * d->d_v, ab + L.wo, base_epi(EPI_F32, y));
 }
 
 }  // extern "C"

@@ -936,4 +936,229 @@ hipError_t launch_attention(const AttnArgs& a_in, bool bf16, hipStream_t s) {
   return (a.n_q == 1 && a.n_hg == 1) ? launch_attn_t<CfgBf16Nt>(a, s) : launch_attn_t<CfgBf16>(a, s);
 }
 
+// ===========================================================================
+// Expanded-form chunked prefill (bf16, d_nope = d_v = 128, d_rope = 64).
+//
+// For long query chunks the scores are cheaper against per-head keys than
+// against the 576-wide latents: every cached latent is up-projected once to
+// k[h] = c W_UK[h] (128) and v[h] = c W_UV[h] (128) (GEMMs, outside this
+// kernel), and each head runs causal softmax attention with 192-wide keys
+// (k[h] | the shared RoPE key of the cache row) and 128-wide values (page
+// "How DeepSeek Rewrote the Transformer", sections 03-04: queries, keys,
+// values and the causal mask per head; page "Multi-Head Latent Attention
+// (MLA)", "The construction": per-head keys and values are up-projections
+// of the latent).
+//
+// A work-group takes 128 queries of one (sequence, head); wave w owns
+// queries 32w..32w+31 and needs nothing from the other waves except the
+// shared key/value tiles:
+//   * 32-key tiles go global -> LDS by buffer-load DMA through a 3-stage
+//     ring, as five 64-column blocks (k[h] 0-63, 64-127, k_pe, v[h] 0-63,
+//     64-127) of 128-byte rows with the decode kernel's chunk swizzle;
+//   * S^T[32 keys x 32 queries] = K_tile . Q^T (12 MFMAs, Q in registers):
+//     a lane holds one query, so the online softmax is in-lane plus one
+//     permlane32 exchange;
+//   * O^T[128 dims x 32 queries] += V_tile^T . P^T: the B operand (P^T) is
+//     the score registers rounded to bf16, the A operand four transposing
+//     LDS reads per 32 dims; the lane again holds one query, so rescaling
+//     and the final normalisation are per lane.
+// ===========================================================================
+constexpr int kFaTile = 32;
+constexpr int kFaBlk = kFaTile * 128;     // one 64-column block of a tile
+constexpr int kFaStage = 5 * kFaBlk;      // K 0-63 | K 64-127 | k_pe | V 0-63 | V 64-127
+constexpr int kFaNst = 3;
+constexpr int kFaOStr = 128 * 2 + 16;     // O staging row: 128 bf16 + pad
+constexpr int kFaLds = kFaNst * kFaStage > 4 * 32 * kFaOStr ? kFaNst * kFaStage : 4 * 32 * kFaOStr;
+
+bool prefill_supported(bool bf16, int d_nope, int d_rope, int d_v) {
+  return bf16 && d_nope == 128 && d_rope == 64 && d_v == 128;
+}
+
+__global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hi = lane >> 5, l32 = lane & 31;
+  const int b = blockIdx.z, h = blockIdx.y, t0 = blockIdx.x * 128;
+  const int kvl = a.kv_len[b];
+  const int tw = t0 + 32 * wave;  // first query of this wave
+  const int t = tw + l32;         // this lane's query
+  const bool qv = t < a.n_q;
+  const size_t orow = (size_t)(b * a.n_q + t) * a.H + h;  // output row of (query, head)
+  if (kvl < a.n_q || kvl > a.s_max) {
+    // the sequence's length is unusable: flag it, poison its outputs
+    if (threadIdx.x == 0) atomicOr(a.err, 4);
+    if (qv && hi == 0) {
+      __bf16* o = reinterpret_cast<__bf16*>(a.vo) + orow * 128;
+      for (int d = 0; d < 128; ++d) o[d] = (__bf16)__builtin_nanf("");
+      if (a.lse) a.lse[orow] = __builtin_nanf("");
+    }
+    return;
+  }
+  const int S = kvl - a.n_q;                        // rows before the chunk
+  const int t_last = min(t0 + 127, a.n_q - 1);
+  const int kend = S + t_last + 1;                  // keys [0, kend) for this block
+  const int ntiles = (kend + kFaTile - 1) / kFaTile;
+  const int wave_kend = tw < a.n_q ? S + min(tw + 31, a.n_q - 1) + 1 : 0;  // keys this wave needs
+  const int qpos = S + t;                           // keys 0 .. qpos are visible to this lane
+
+  // Q^T fragments (B operand): query t, dims 16 kb + 8 hi .. +7
+  bf16x8 qf[12];
+  {
+    const __bf16* qp = reinterpret_cast<const __bf16*>(a.qe) + (qv ? orow : (size_t)h) * 192 + 8 * hi;
+#pragma unroll
+    for (int kb = 0; kb < 12; ++kb) qf[kb] = qv ? load_frag<__bf16>(qp + 16 * kb) : Mfma<__bf16>::zero();
+  }
+
+  // DMA: wave w fills rows 8w + lane/8 of each block; the lane's LDS slot is
+  // physical chunk lane%8 of its row, i.e. logical chunk c
+  const int dr = 8 * wave + (lane >> 3);
+  const int dc = (lane & 7) ^ swz(dr);
+  const int kv_row_bytes = a.H * 256;
+  auto issue = [&](int it, unsigned char* st) {
+    const int k0 = it * kFaTile;
+    const int rows = it < ntiles ? min(kFaTile, kend - k0) : 0;
+    const size_t r0 = (size_t)b * a.s_max + k0;
+    const __amdgpu_buffer_rsrc_t rk =
+        make_rsrc(reinterpret_cast<const __bf16*>(a.ke) + (r0 * a.H + h) * 128, rows * kv_row_bytes);
+    const __amdgpu_buffer_rsrc_t rv =
+        make_rsrc(reinterpret_cast<const __bf16*>(a.ve) + (r0 * a.H + h) * 128, rows * kv_row_bytes);
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(reinterpret_cast<const __bf16*>(a.pool) + r0 * 576 + 512, rows * 1152);
+    const int ko = dr * kv_row_bytes + dc * 16;
+    unsigned char* w0 = st + wave * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, MLA_LDS_PTR(w0 + 0 * kFaBlk), 16, ko, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, MLA_LDS_PTR(w0 + 1 * kFaBlk), 16, ko + 128, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rp, MLA_LDS_PTR(w0 + 2 * kFaBlk), 16, dr * 1152 + dc * 16, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, MLA_LDS_PTR(w0 + 3 * kFaBlk), 16, ko, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, MLA_LDS_PTR(w0 + 4 * kFaBlk), 16, ko + 128, 0, 0, 0);
+  };
+  constexpr int kLoads = 5;  // DMA instructions per tile and wave
+
+  // lane-constant LDS offsets: score A fragments (key row l32, chunk pair
+  // 2u + hi of a block) and the transposing V reads (rows 16 ks + 4 hi +
+  // 8 h2 + s/4 of column tile t, s = lane%16)
+  int s_base[4], trb[2][2];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) s_base[u] = l32 * 128 + 16 * ((2 * u + hi) ^ swz(l32));
+  {
+    const int g = lane >> 4, sl = lane & 15;
+    const int c_low = 2 * (g & 1) + ((sl & 3) >> 1);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+        trb[tt][h2] = (4 * hi + 8 * h2 + (sl >> 2)) * 128 + 64 * (tt ^ ((sl >> 3) & 1)) +
+                      16 * (c_low ^ (hi + 2 * h2)) + 8 * (sl & 1);
+  }
+
+  issue(0, smem);
+  issue(1, smem + kFaStage);
+  float m_run = -1e30f, l_run = 0.f;
+  f32x16 O[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) O[dt] = f32x16{};
+  typedef short v4s __attribute__((ext_vector_type(4)));
+
+  for (int it = 0; it < ntiles; ++it) {
+    vm_wait<(kFaNst - 2) * kLoads>();
+    lds_barrier();
+    issue(it + 2, smem + ((it + 2) % kFaNst) * kFaStage);
+    const int k0 = it * kFaTile;
+    if (k0 >= wave_kend) continue;  // every key of the tile is after this wave's queries
+    const unsigned char* tb = smem + (it % kFaNst) * kFaStage;
+
+    // ---- S^T = K . Q^T ---------------------------------------------------
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int kb = 0; kb < 12; ++kb) {
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(tb + (kb >> 2) * kFaBlk + s_base[kb & 3]);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kb], s, 0, 0, 0);
+    }
+    // ---- online softmax for query t (register r: key k0 + 8(r/4) + 4hi + r%4)
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[r] = s[r];
+    if (k0 + kFaTile - 1 > S + tw) {  // uniform: the tile reaches past the wave's first query
+      const int lim = qpos - k0 - 4 * hi;  // visible: 8(r/4) + r%4 <= lim
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r >> 2) + (r & 3) > lim) x[r] = -INFINITY;
+    }
+    float mraw = x[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mraw = fmaxf(mraw, x[r]);
+    const float mloc = max_xor32(mraw) * a.scale_log2;
+    if (mloc > m_run + kRescaleSlack) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mloc);
+      m_run = mloc;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) O[dt][r] *= alpha;
+    }
+    float psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      x[r] = __builtin_amdgcn_exp2f(fmaf(x[r], a.scale_log2, -m_run));
+      psum += x[r];
+    }
+    l_run += sum_xor32(psum);
+    bf16x8 pf[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pf[ks][j] = (__bf16)x[8 * ks + j];
+    // ---- O^T += V^T . P^T -------------------------------------------------
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        v4s vv[2];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+          vv[h2] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<__attribute__((address_space(3))) v4s*>(
+              MLA_LDS_PTR(tb + (3 + (dt >> 1)) * kFaBlk + trb[dt & 1][h2] + ks * 16 * 128)));
+        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pf[ks], O[dt], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- finalise: normalise, stage [32 queries][128 dims] per wave, store rows
+  vm_wait<0>();  // the DMA issued past the last tile (zeros) may still land in the ring
+  lds_barrier();
+  const float inv = 1.f / l_run;
+  unsigned char* ost = smem + wave * 32 * kFaOStr;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      __bf16 v4[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v4[u] = (__bf16)(O[dt][4 * q4 + u] * inv);
+      *reinterpret_cast<uint2*>(ost + l32 * kFaOStr + (32 * dt + 8 * q4 + 4 * hi) * 2) =
+          *reinterpret_cast<const uint2*>(v4);
+    }
+  lds_barrier();
+  for (int i = lane; i < 32 * 16; i += 64) {
+    const int qr = i >> 4, ch = i & 15, tq = tw + qr;
+    if (tq < a.n_q)
+      *reinterpret_cast<uint4*>(reinterpret_cast<__bf16*>(a.vo) + ((size_t)(b * a.n_q + tq) * a.H + h) * 128 + ch * 8) =
+          *reinterpret_cast<const uint4*>(ost + qr * kFaOStr + ch * 16);
+  }
+  if (qv && hi == 0 && a.lse) a.lse[orow] = (m_run + __log2f(l_run)) * 0.69314718055994531f;
+}
+
+hipError_t launch_prefill_attention(const PrefillArgs& a, hipStream_t s) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_attn_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kFaLds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(prefill_attn_kernel, dim3((a.n_q + 127) / 128, a.H, a.B), dim3(256), kFaLds, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace mla

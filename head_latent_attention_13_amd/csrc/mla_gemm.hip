@@ -1026,6 +1026,8 @@ static hipError_t pack_factored_t(const AbsorbArgs& a, hipStream_t s) {
   if ((e = pack_one<T>(a, PACK_PLAIN, a.d_q_latent, a.H * a.d_rope, a.P_QR, a.W_QR, (long)a.H * a.d_rope, s)))
     return e;
   if ((e = pack_one<T>(a, PACK_UKT, a.d_nope, a.H * a.d_latent, a.P_UKT, nullptr, 0, s)) != hipSuccess) return e;
+  if ((e = pack_one<T>(a, PACK_PLAIN, a.d_latent, a.H * a.d_nope, a.P_UK, a.W_UK, (long)a.H * a.d_nope, s)))
+    return e;
   if ((e = pack_one<T>(a, PACK_PLAIN, a.d_latent, a.H * a.d_v, a.P_UV, a.W_UV, (long)a.H * a.d_v, s)))
     return e;
   return pack_one<T>(a, PACK_PLAIN, a.H * a.d_v, a.d_model, a.P_WO, a.W_O, (long)a.d_model, s);

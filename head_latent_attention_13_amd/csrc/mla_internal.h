@@ -74,7 +74,7 @@ struct AbsorbArgs {
   const void *W_DQ, *W_UQ, *W_QR, *W_DKV, *W_KR, *W_UK, *W_UV, *W_O;
   void *P_KV, *P_DQ, *P_QC, *P_O;   // packed outputs (merged form: all four)
   int factored;                      // factored form: P_KV, P_DQ and these five
-  void *P_UQ, *P_QR, *P_UKT, *P_UV, *P_WO;
+  void *P_UQ, *P_QR, *P_UKT, *P_UK, *P_UV, *P_WO;
 };
 hipError_t launch_absorb(const AbsorbArgs& a, bool bf16, hipStream_t s);
 
@@ -106,5 +106,25 @@ int attn_head_group(bool bf16);  // heads per attention work-group
 int attn_tile();
 size_t attn_sched_ints(int U, int G);  // ints of plan storage for U streams, G work-groups
 hipError_t launch_attention(const AttnArgs& a, bool bf16, hipStream_t s);
+
+// ------------------------------------------------ expanded-form prefill ----
+// Causal attention of n_q new query tokens per sequence over per-head keys
+// and values up-projected from the latent cache (bf16; d_nope = d_v = 128,
+// d_rope = 64).  Query row m = b*n_q + t sits at position kv_len[b]-n_q+t and
+// sees keys 0 .. that position.
+struct PrefillArgs {
+  const void* qe;         // [B*n_q][H][192] bf16: q_nope | RoPE'd q_pe
+  const void* ke;         // [B*s_max][H*128] bf16: c_i W_UK[h]
+  const void* ve;         // [B*s_max][H*128] bf16: c_i W_UV[h]
+  const void* pool;       // [B][s_max][576] bf16 contiguous cache (k_pe at 512..575)
+  const int32_t* kv_len;  // [B]
+  int B, n_q, H, s_max;
+  float scale_log2;       // softmax scale * log2(e)
+  void* vo;               // [B*n_q][H*128] bf16 out: softmax . V per head
+  float* lse;             // [B*n_q][H] out or null (natural log)
+  int32_t* err;           // bit 4: kv_len outside [n_q, s_max]
+};
+bool prefill_supported(bool bf16, int d_nope, int d_rope, int d_v);
+hipError_t launch_prefill_attention(const PrefillArgs& a, hipStream_t s);
 
 }  // namespace mla

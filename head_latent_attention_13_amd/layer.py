@@ -45,5 +45,20 @@ class MLALayer:
     def out_proj(self, o_lat, n_tok, y, stream=None):
         L.mla_out_proj(self.dims, self.absorbed, o_lat, n_tok, y, self.workspace, stream)
 
+    def prefill_expanded(self, x, kv_len, batch, n_q, cache: L.Cache, y, lse: Optional[torch.Tensor] = None,
+                         stream=None):
+        """Expanded-form chunked prefill (factored weights, contiguous cache);
+        its workspace, sized for (batch, n_q, cache.s_max), is kept until a
+        larger one is needed."""
+        need = L.mla_prefill_workspace_size(self.dims, batch, n_q, cache.s_max)
+        if getattr(self, "pf_workspace", None) is None or self.pf_workspace.numel() < need:
+            self.pf_workspace = torch.zeros(need, dtype=torch.uint8, device=self.device)
+        L.mla_prefill_expanded(self.dims, self.absorbed, x, kv_len, batch, n_q, cache, y, lse, self.pf_workspace,
+                               stream)
+
+    def prefill_error(self, stream=None) -> int:
+        ws = getattr(self, "pf_workspace", None)
+        return 0 if ws is None else L.mla_read_device_error(ws, stream)
+
     def device_error(self, stream=None) -> int:
         return L.mla_read_device_error(self.workspace, stream)

@@ -145,11 +145,13 @@ const char *mla_version(void);
  *                f >= d_L : W_QR[:, h, f - d_L]
  *   [3] W_UVO  : K = H * d_L,  N = d_model    row h*d_L + c:
  *                (W_UV[h] W_O[h])[c, :]  (merged, output side)
- * Factored form: [0] and [1] as above; region [2] holds three matrices and
+ * Factored form: [0] and [1] as above; region [2] holds four matrices and
  * region [3] two, each starting at a 256-byte boundary in this order:
  *   [2] W_UQ  : K = d_LQ,   N = H * d_nope   column h*d_nope + f: W_UQ[:, h, f]
  *       W_QR  : K = d_LQ,   N = H * d_rope   column h*d_rope + f: W_QR[:, h, f]
  *       W_UKT : K = d_nope, N = H * d_L      column h*d_L + c:    W_UK[c, h, :]
+ *       W_UK  : K = d_L,    N = H * d_nope   column h*d_nope + f: W_UK[:, h, f]
+ *               (keys of the expanded prefill)
  *   [3] W_UV  : K = d_L,    N = H * d_v      column h*d_v + f:    W_UV[:, h, f]
  *       W_O   : K = H*d_v,  N = d_model      row h*d_v + f:       W_O[h, f, :]
  * Packed order of a logical K x N matrix W (y = x W): element (k, n) sits at
@@ -228,6 +230,34 @@ mla_status mla_decode(const mla_dims *dims, const void *absorbed, const void *x,
  *   o_lat [n_tok, H, d_latent] fp32;  y [n_tok, d_model] fp32 out. */
 mla_status mla_out_proj(const mla_dims *dims, const void *absorbed, const float *o_lat, int32_t n_tok, float *y,
                         void *workspace, size_t ws_bytes, void *stream);
+
+/* Workspace bytes needed by mla_prefill_expanded for up to `batch`
+ * sequences of `n_q` new tokens over a contiguous cache of s_max rows per
+ * sequence (host only).  The first 256 bytes hold the device error word, as
+ * in mla_workspace_size: zero the workspace once before first use. */
+mla_status mla_prefill_workspace_size(const mla_dims *dims, int32_t batch, int32_t n_q, int32_t s_max,
+                                      size_t *bytes);
+
+/* Chunked prefill in the expanded form (for long query chunks, where the
+ * attention is bound by matrix throughput): every cached latent c_i is
+ * up-projected to per-head keys k_i[h] = c_i W_UK[h] and values
+ * v_i[h] = c_i W_UV[h]; each head runs causal softmax attention with the
+ * query [c_Q W_UQ[h] | RoPE_t(c_Q W_QR[h])] against [k_i[h] | k_pe_i]; then
+ * y = sum_h o[h] W_O[h] (page "How DeepSeek Rewrote the Transformer",
+ * sections 03-04; page "Multi-Head Latent Attention (MLA)", "The
+ * construction").  The same function as mla_decode + mla_out_proj.
+ * Needs dims->weight_form == MLA_WEIGHTS_FACTORED, dtype bf16, d_nope =
+ * d_v = 128, d_rope = 64 (else MLA_ERR_UNSUPPORTED) and a contiguous cache
+ * (page_table NULL) into which the n_q new rows are already appended.
+ *   x      [batch * n_q, d_model] bf16; kv_len [batch] int32 as in mla_attention
+ *   y      [batch * n_q, d_model] fp32 out
+ *   lse    [batch * n_q, H] fp32 out or NULL (natural log, scaled scores)
+ * The per-head keys and values of all batch * s_max cache slots live in the
+ * workspace (mla_prefill_workspace_size).  A kv_len outside [n_q, s_max]
+ * sets error bit 4 and makes that sequence's outputs NaN. */
+mla_status mla_prefill_expanded(const mla_dims *dims, const void *absorbed, const void *x, const int32_t *kv_len,
+                                int32_t batch, int32_t n_q, const mla_cache *cache, float *y, float *lse,
+                                void *workspace, size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

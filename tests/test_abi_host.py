@@ -70,7 +70,7 @@ def test_absorbed_layout_pads_fp32_tiny():
 
 
 def test_factored_layout_holds_the_repacked_factors():
-    """Factored form: region 2 = W_UQ | W_QR | W_UK^T, region 3 = W_UV | W_O,
+    """Factored form: region 2 = W_UQ | W_QR | W_UK^T | W_UK, region 3 = W_UV | W_O,
     each matrix at a 256-byte boundary; about a third of the merged bytes
     at the DeepSeek-V2 shapes."""
     _lib()
@@ -78,13 +78,13 @@ def test_factored_layout_holds_the_repacked_factors():
     offs, sizes, total = mla.mla_absorbed_layout(d)
     R, H, e = 576, 128, 2
     al = lambda x: -(-x // 256) * 256
-    uq, qr, ukt = 1536 * H * 128 * e, 1536 * H * 64 * e, 128 * H * 512 * e
+    uq, qr, ukt, uk = 1536 * H * 128 * e, 1536 * H * 64 * e, 128 * H * 512 * e, 512 * H * 128 * e
     uv, wo = 512 * H * 128 * e, H * 128 * 5120 * e
     assert sizes[:2] == [5120 * R * e, 5120 * 1536 * e]
-    assert sizes[2] == al(uq) + al(qr) + ukt and sizes[3] == al(uv) + wo
+    assert sizes[2] == al(uq) + al(qr) + al(ukt) + uk and sizes[3] == al(uv) + wo
     assert offs[3] == offs[2] + al(sizes[2]) and total == offs[3] + al(sizes[3])
     _, msizes, mtotal = mla.mla_absorbed_layout(v2_dims())
-    assert total < 0.35 * mtotal
+    assert total < 0.37 * mtotal
     # tiny fp32 shape: padded columns (N = 4 * 8 = 32 needs none; K = 16 none)
     t = mla.make_dims(64, 4, 32, 48, 16, 8, 16, "f32", form="factored")
     offs, sizes, total = mla.mla_absorbed_layout(t)
@@ -103,6 +103,22 @@ def test_factored_dims_checked(field, value, code):
     with pytest.raises(mla.MLAError) as e:
         mla.mla_workspace_size(d, 16, 1)
     assert e.value.status == code
+
+
+def test_prefill_checks():
+    """Expanded prefill: factored bf16 weights of the V2/V3 head shape only;
+    its workspace holds the per-head keys and values of every cache slot."""
+    _lib()
+    f = mla.make_dims(7168, 128, 512, 1536, 128, 64, 128, "bf16", form="factored")
+    n = mla.mla_prefill_workspace_size(f, 2, 1024, 5120)
+    assert n > 2 * 2 * 5120 * 128 * 128 * 2  # keys + values of 10240 slots
+    assert mla.mla_prefill_workspace_size(f, 2, 1024, 6000) > n
+    for bad, code in ((mla.make_dims(7168, 128, 512, 1536, 128, 64, 128, "bf16"), -2),          # merged form
+                      (mla.make_dims(64, 4, 32, 48, 16, 8, 16, "f32", form="factored"), -2),  # fp32 shape
+                      (f, -1)):                                                              # s_max 0
+        with pytest.raises(mla.MLAError) as e:
+            mla.mla_prefill_workspace_size(bad, 2, 1024, 0 if bad is f else 5120)
+        assert e.value.status == code
 
 
 def test_workspace_size_grows_with_batch():

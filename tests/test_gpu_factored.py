@@ -73,6 +73,7 @@ def test_factored_tiny_f32_end_to_end_and_packing():
     uq, at = take(offs[2], cfg.d_q_latent, H * cfg.d_nope)
     qr, at = take(at, cfg.d_q_latent, H * cfg.d_rope)
     ukt, at = take(at, cfg.d_nope, H * L)
+    uk, at = take(at, L, H * cfg.d_nope)
     assert at == offs[3]
     uv, at = take(offs[3], L, H * cfg.d_v)
     wo, at = take(at, H * cfg.d_v, cfg.d_model)
@@ -80,6 +81,7 @@ def test_factored_tiny_f32_end_to_end_and_packing():
     assert np.array_equal(uq, W["W_UQ"].reshape(cfg.d_q_latent, -1))
     assert np.array_equal(qr, W["W_QR"].reshape(cfg.d_q_latent, -1))
     assert np.array_equal(ukt.reshape(cfg.d_nope, H, L), W["W_UK"].transpose(2, 1, 0))
+    assert np.array_equal(uk, W["W_UK"].reshape(L, -1))
     assert np.array_equal(uv, W["W_UV"].reshape(L, -1))
     assert np.array_equal(wo, W["W_O"].reshape(H * cfg.d_v, cfg.d_model))
     cache, pool = contiguous_cache(cfg, [np.zeros((0, R), np.float32)], S + cfg.n_q)
