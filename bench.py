@@ -41,6 +41,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--form", choices=("merged", "factored"), default="merged",
                    help="absorbed weights: merged products (default) or the factors applied at run time")
+    p.add_argument("--prefill", choices=("absorbed", "expanded"), default="absorbed",
+                   help="expanded: the step is append + mla_prefill_expanded (factored weights, contiguous cache; "
+                        "the V3 chunked-prefill workload)")
     p.add_argument("--copies", type=int, default=4,
                    help="input sets (absorbed weights, cache, activations) rotated over the steps, so that no "
                         "step finds its inputs in the 256 MB last-level cache")
@@ -188,6 +191,11 @@ def main():
 
     torch.cuda.set_device(0)
     cfg = config(args.config)
+    if args.prefill == "expanded":
+        if cfg.paged:
+            print("--prefill expanded needs a contiguous cache", file=sys.stderr)
+            sys.exit(2)
+        args.form = "factored"
     case = make_case(cfg, args.config, history="rows")
     B, n_q, H, R = cfg.batch, cfg.n_q, cfg.n_heads, cfg.row
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
@@ -244,7 +252,9 @@ def main():
     o_lats = [torch.empty(B * n_q, H, cfg.d_latent, dtype=torch.float32, device="cuda") for _ in range(NC)]
     ys = [torch.empty(B * n_q, cfg.d_model, dtype=torch.float32, device="cuda") for _ in range(NC)]
 
-    calls = ("mla_compress_append", "mla_q_proj", "mla_attention", "mla_out_proj")
+    expanded = args.prefill == "expanded"
+    calls = (("mla_compress_append", "mla_prefill_expanded") if expanded else
+             ("mla_compress_append", "mla_q_proj", "mla_attention", "mla_out_proj"))
 
     def step(k, evs=None):
         def mark(i):
@@ -255,6 +265,10 @@ def main():
         mark(0)
         ly.append(xx, poss[j], B, n_q, cc)
         mark(1)
+        if expanded:
+            ly.prefill_expanded(xx, kvs[j], B, n_q, cc, ys[j])
+            mark(2)
+            return
         ly.q_proj(xx, kvs[j], B, n_q, qq)
         mark(2)
         ly.attention(qq, kvs[j], B, n_q, cc, ol)
@@ -278,13 +292,13 @@ def main():
     # per-call breakdown: a second pass with an event between the calls (the
     # markers themselves cost a few microseconds per call, so this pass is
     # not used for the step time)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
     for k in range(args.steps):
         step(k, ev[k])
     torch.cuda.synchronize()
     per_call_ms = {c: float(np.mean([ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(args.steps)]))
                    for i, c in enumerate(calls)}
-    assert all(ly.device_error() == 0 for ly in layers)
+    assert all(ly.device_error() == 0 and ly.prefill_error() == 0 for ly in layers)
 
     # ---- algorithmic bytes / flops per call (one step) ------------------
     eb = 2 if cfg.dtype == "bf16" else 4
@@ -303,7 +317,19 @@ def main():
         "mla_out_proj": {"bytes": wbytes[3] + M * H * cfg.d_latent * 4 + M * cfg.d_model * 4,
                          "flops": 2 * M * H * cfg.d_latent * cfg.d_model},
     }
-    if args.form == "factored":
+    if expanded:
+        # queries, per-head keys/values of every cache slot (written, read back), causal attention per
+        # head with 192-wide keys and 128-wide values, the W_O product
+        s_slots = B * cache.s_max
+        kv_bytes = 2 * s_slots * H * (cfg.d_nope + cfg.d_v) * eb
+        algo["mla_prefill_expanded"] = {
+            "bytes": wbytes[1] + wbytes[2] + wbytes[3] + M * cfg.d_model * eb + s_slots * R * eb + kv_bytes
+                     + M * cfg.d_model * 4,
+            "flops": 2 * M * (cfg.d_model * cfg.d_q_latent + cfg.d_q_latent * H * (cfg.d_nope + cfg.d_rope))
+                     + 2 * s_slots * cfg.d_latent * H * (cfg.d_nope + cfg.d_v)
+                     + 2 * H * pairs * (cfg.d_nope + cfg.d_rope + cfg.d_v)
+                     + 2 * M * H * cfg.d_v * cfg.d_model}
+    if args.form == "factored" and not expanded:
         # the factors plus the intermediates c_Q W_UQ and o_lat W_UV (written, read back)
         algo["mla_q_proj"] = {
             "bytes": wbytes[1] + wbytes[2] + M * cfg.d_model * eb + M * H * R * eb + 2 * M * H * cfg.d_nope * eb,
@@ -334,7 +360,7 @@ def main():
     else:
         roofline = {"bound": "mfma", "achieved": d["TFLOP_s"], "peak": mfma_peak, "unit": "TFLOP/s",
                     "frac": round(d["TFLOP_s"] / mfma_peak, 4), "traffic": traffic, "kernel": dom}
-    att = kernels["mla_attention"]
+    att = kernels["mla_prefill_expanded" if expanded else "mla_attention"]
 
     out = {
         "metric": "MLA decode tokens/s + latent-cache HBM GB/s & MFMA % of peak, 1 MI355X",
@@ -353,9 +379,10 @@ def main():
                                                                       else int(cfg.cached)),
                    "new_tokens": n_q, "heads": H, "d_latent": cfg.d_latent, "d_rope": cfg.d_rope,
                    "d_model": cfg.d_model, "cache": "paged" if cfg.paged else "contiguous",
-                   "weights": args.form},
+                   "weights": args.form, "prefill": args.prefill},
         "roofline": roofline,
-        "latent_cache_GB_s": round(cache_bytes / (per_call_ms["mla_attention"] * 1e-3) / 1e9, 1),
+        "latent_cache_GB_s": round(cache_bytes / (per_call_ms["mla_prefill_expanded" if expanded else "mla_attention"]
+                                                   * 1e-3) / 1e9, 1),
         "attention_mfma_pct": round(100 * att["mfma_frac"], 2),
         "attention_roofline_frac": att["roofline_frac"],
         # measured from the allocation (paged pools round up to whole pages)
@@ -363,7 +390,7 @@ def main():
         "kernels": kernels,
         # rocprofv3 counters (SQ_INSTS_VALU_MFMA_MOPS_BF16 calibrated on a product of known size,
         # SQ_VALU_MFMA_BUSY_CYCLES / GRBM_GUI_ACTIVE), when taken on these kernel sources
-        "mfma_counters": (measured_mfma(cfg.name) if args.form == "merged" else None),
+        "mfma_counters": (measured_mfma(cfg.name) if args.form == "merged" and not expanded else None),
         "absorb_ms_once": round(absorb_ms, 3),
     }
     if not args.no_cpu_baseline:
