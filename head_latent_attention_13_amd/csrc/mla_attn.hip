@@ -974,12 +974,101 @@ bool prefill_supported(bool bf16, int d_nope, int d_rope, int d_v) {
   return bf16 && d_nope == 128 && d_rope == 64 && d_v == 128;
 }
 
+// One 32-key tile of the prefill: the DMA of a later tile into `dma_st`,
+// then (if any key of the tile is visible to the wave) scores, online
+// softmax and the PV update from `tb`.  Both stage pointers are restrict:
+// within one call the stage being filled and the stage being read never
+// overlap, which lets the compiler's wait insertion keep the DMA in flight
+// while the tile is read.  The fragments of each phase are read from LDS
+// before its MFMAs.
+template <class Issue>
+__device__ __forceinline__ void prefill_tile(const PrefillArgs& a, const Issue& issue, unsigned char* __restrict__ dma_st,
+                                             const unsigned char* __restrict__ tb, int it_issue, int k0, bool live,
+                                             int wave_q0, int qpos, int hi, const int (&s_base)[4],
+                                             const int (&trb)[2][2], const bf16x8 (&qf)[12], float& m_run,
+                                             float& l_run, f32x16 (&O)[4]) {
+  issue(it_issue, dma_st);
+  if (!live) return;  // every key of the tile is after this wave's queries
+  // ---- S^T = K . Q^T -----------------------------------------------------
+  bf16x8 ka[12];
+#pragma unroll
+  for (int kb = 0; kb < 12; ++kb) ka[kb] = *reinterpret_cast<const bf16x8*>(tb + (kb >> 2) * kFaBlk + s_base[kb & 3]);
+  __builtin_amdgcn_sched_barrier(0);  // keep the twelve reads ahead of the chain
+  f32x16 s = f32x16{};
+#pragma unroll
+  for (int kb = 0; kb < 12; ++kb) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kb], qf[kb], s, 0, 0, 0);
+  // ---- online softmax for this lane's query (register r: key k0 + 8(r/4) + 4hi + r%4)
+  float x[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) x[r] = s[r];
+  if (k0 + kFaTile - 1 > wave_q0) {  // uniform: the tile reaches past the wave's first query
+    const int lim = qpos - k0 - 4 * hi;  // visible: 8(r/4) + r%4 <= lim
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (8 * (r >> 2) + (r & 3) > lim) x[r] = -INFINITY;
+  }
+  float mraw = x[0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) mraw = fmaxf(mraw, x[r]);
+  const float mloc = max_xor32(mraw) * a.scale_log2;
+  if (mloc > m_run + kRescaleSlack) {
+    const float alpha = __builtin_amdgcn_exp2f(m_run - mloc);
+    m_run = mloc;
+    l_run *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) O[dt][r] *= alpha;
+  }
+  float psum = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    x[r] = __builtin_amdgcn_exp2f(fmaf(x[r], a.scale_log2, -m_run));
+    psum += x[r];
+  }
+  l_run += sum_xor32(psum);
+  bf16x8 pf[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pf[ks][j] = (__bf16)x[8 * ks + j];
+  // ---- O^T += V^T . P^T ----------------------------------------------------
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  v4s vv[4][2][2];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+        vv[dt][ks][h2] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<__attribute__((address_space(3))) v4s*>(
+            MLA_LDS_PTR(const_cast<unsigned char*>(tb) + (3 + (dt >> 1)) * kFaBlk + trb[dt & 1][h2] + ks * 16 * 128)));
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv[dt][ks]), pf[ks], O[dt], 0, 0, 0);
+}
+
 __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hi = lane >> 5, l32 = lane & 31;
-  const int b = blockIdx.z, h = blockIdx.y, t0 = blockIdx.x * 128;
+  // Work-groups are handed to the eight XCDs round-robin by linear id.  The
+  // query blocks of one (sequence, head) read the same keys and values, so
+  // they are renumbered to run together on one XCD and share its L2.
+  int qb, h, b;
+  {
+    const int gx = gridDim.x, gy = gridDim.y, T = gx * gy * gridDim.z;
+    const int id = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+    const int L = (T & 7) ? id : (id & 7) * (T >> 3) + (id >> 3);
+    qb = L % gx;
+    h = (L / gx) % gy;
+    b = L / (gx * gy);
+  }
+  const int t0 = qb * 128;
   const int kvl = a.kv_len[b];
   const int tw = t0 + 32 * wave;  // first query of this wave
   const int t = tw + l32;         // this lane's query
@@ -1057,71 +1146,12 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillArgs a) {
   f32x16 O[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) O[dt] = f32x16{};
-  typedef short v4s __attribute__((ext_vector_type(4)));
 
   for (int it = 0; it < ntiles; ++it) {
     vm_wait<(kFaNst - 2) * kLoads>();
     lds_barrier();
-    issue(it + 2, smem + ((it + 2) % kFaNst) * kFaStage);
-    const int k0 = it * kFaTile;
-    if (k0 >= wave_kend) continue;  // every key of the tile is after this wave's queries
-    const unsigned char* tb = smem + (it % kFaNst) * kFaStage;
-
-    // ---- S^T = K . Q^T ---------------------------------------------------
-    f32x16 s = f32x16{};
-#pragma unroll
-    for (int kb = 0; kb < 12; ++kb) {
-      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(tb + (kb >> 2) * kFaBlk + s_base[kb & 3]);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kb], s, 0, 0, 0);
-    }
-    // ---- online softmax for query t (register r: key k0 + 8(r/4) + 4hi + r%4)
-    float x[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) x[r] = s[r];
-    if (k0 + kFaTile - 1 > S + tw) {  // uniform: the tile reaches past the wave's first query
-      const int lim = qpos - k0 - 4 * hi;  // visible: 8(r/4) + r%4 <= lim
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (8 * (r >> 2) + (r & 3) > lim) x[r] = -INFINITY;
-    }
-    float mraw = x[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mraw = fmaxf(mraw, x[r]);
-    const float mloc = max_xor32(mraw) * a.scale_log2;
-    if (mloc > m_run + kRescaleSlack) {
-      const float alpha = __builtin_amdgcn_exp2f(m_run - mloc);
-      m_run = mloc;
-      l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) O[dt][r] *= alpha;
-    }
-    float psum = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      x[r] = __builtin_amdgcn_exp2f(fmaf(x[r], a.scale_log2, -m_run));
-      psum += x[r];
-    }
-    l_run += sum_xor32(psum);
-    bf16x8 pf[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) pf[ks][j] = (__bf16)x[8 * ks + j];
-    // ---- O^T += V^T . P^T -------------------------------------------------
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        v4s vv[2];
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2)
-          vv[h2] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<__attribute__((address_space(3))) v4s*>(
-              MLA_LDS_PTR(tb + (3 + (dt >> 1)) * kFaBlk + trb[dt & 1][h2] + ks * 16 * 128)));
-        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pf[ks], O[dt], 0, 0, 0);
-      }
-    }
+    prefill_tile(a, issue, smem + ((it + 2) % kFaNst) * kFaStage, smem + (it % kFaNst) * kFaStage, it + 2,
+                 it * kFaTile, it * kFaTile < wave_kend, S + tw, qpos, hi, s_base, trb, qf, m_run, l_run, O);
   }
 
   // ---- finalise: normalise, stage [32 queries][128 dims] per wave, store rows
