@@ -138,14 +138,32 @@ AbsLayout abs_layout(const mla_dims* d) {
 
 // ---------------------------------------------------------- workspace ----
 struct WsLayout {
-  size_t err, q, cq, qn, vo, part, tile_off, attn_o, attn_lse, total;
+  size_t err, q, cq, qn, vo, ob, part, tile_off, attn_o, attn_lse, total;
   GemmPlan g_app, g_cq, g_q, g_out;
   // factored form: q_nope = c_Q W_UQ, q_pe, q_lat = q_nope[h] W_UK[h]^T,
   // v = o_lat[h] W_UV[h], y = v W_O
   GemmPlan g_qn, g_qr, g_qk, g_ov, g_oo;
   int G, V;
   bool plans_ok;
+  // o_lat goes through a bf16 copy (ob) before the output projection: set
+  // when the fp32-A plan would be the 256 x 256 tiling, whose fp32 stages
+  // leave LDS room for three ring slots only; the bf16-A plan replaces it
+  bool stage_o;
 };
+
+// The fp32-A plan, or the bf16-A plan over a staged copy (stage_o) when the
+// fp32 one is the 256 x 256 tiling.
+static GemmPlan plan_o(bool bf, int M, int K, int N, int ncu, int gt, int gs, bool* staged) {
+  GemmPlan g = plan_gemm(M, K, N, bf, true, ncu, gt, gs);
+  if (bf && g.tiled == 1 && g.MT == 4) {
+    const GemmPlan b = plan_gemm(M, K, N, bf, false, ncu, gt, gs);
+    if (b.tiled == 1) {
+      *staged = true;
+      return b;
+    }
+  }
+  return g;
+}
 
 WsLayout ws_layout(const mla_dims* d, int batch, int n_q) {
   WsLayout W{};
@@ -157,7 +175,7 @@ WsLayout ws_layout(const mla_dims* d, int batch, int n_q) {
   size_t part = std::max(W.g_app.part_bytes, W.g_cq.part_bytes);
   if (!factored(d)) {
     W.g_q = plan_gemm(M, d->d_q_latent, H * R, bf, false, ncu);
-    W.g_out = plan_gemm(M, H * d->d_latent, d->d_model, bf, true, ncu);
+    W.g_out = plan_o(bf, M, H * d->d_latent, d->d_model, ncu, 0, 0, &W.stage_o);
     part = std::max(part, std::max(W.g_q.part_bytes, W.g_out.part_bytes));
     W.plans_ok = true;
   } else {
@@ -165,7 +183,7 @@ WsLayout ws_layout(const mla_dims* d, int batch, int n_q) {
     W.g_qr = plan_gemm(M, d->d_q_latent, H * d->d_rope, bf, false, ncu);
     // per-head products: head h's output tiles read A columns h*K ..
     W.g_qk = plan_gemm(M, d->d_nope, H * d->d_latent, bf, false, ncu, d->d_latent / 16, d->d_nope);
-    W.g_ov = plan_gemm(M, d->d_latent, H * d->d_v, bf, true, ncu, d->d_v / 16, d->d_latent);
+    W.g_ov = plan_o(bf, M, d->d_latent, H * d->d_v, ncu, d->d_v / 16, d->d_latent, &W.stage_o);
     W.g_oo = plan_gemm(M, H * d->d_v, d->d_model, bf, false, ncu);
     for (const GemmPlan* g : {&W.g_qn, &W.g_qr, &W.g_qk, &W.g_ov, &W.g_oo}) part = std::max(part, g->part_bytes);
     W.plans_ok = W.g_qk.tiled >= 0 && W.g_ov.tiled >= 0;
@@ -179,6 +197,9 @@ WsLayout ws_layout(const mla_dims* d, int batch, int n_q) {
   if (factored(d)) {
     W.qn = o; o = align256(o + (size_t)M * H * d->d_nope * esize(d));
     W.vo = o; o = align256(o + (size_t)M * H * d->d_v * esize(d));
+  }
+  if (W.stage_o) {
+    W.ob = o; o = align256(o + (size_t)M * H * d->d_latent * 2);
   }
   W.part = o; o = align256(o + part);
 
@@ -511,13 +532,19 @@ mla_status mla_out_proj(const mla_dims* d, const void* absorbed, const float* o_
   const AbsLayout L = abs_layout(d);
   unsigned char* ws = reinterpret_cast<unsigned char*>(workspace);
   const unsigned char* ab = reinterpret_cast<const unsigned char*>(absorbed);
+  const void* a_op = o_lat;
+  if (W.stage_o) {
+    const hipError_t e = launch_f32_to_bf16(o_lat, ws + W.ob, (size_t)n_tok * d->n_heads * d->d_latent, s);
+    if (e != hipSuccess) return hip_fail(e, "o_lat conversion");
+    a_op = ws + W.ob;
+  }
   if (!factored(d))
-    return run_gemm(W, G_OUT, W.g_out, bf, true, o_lat, d->n_heads * d->d_latent, ab + L.off[3], ws,
+    return run_gemm(W, G_OUT, W.g_out, bf, !W.stage_o, a_op, d->n_heads * d->d_latent, ab + L.off[3], ws,
                     base_epi(EPI_F32, y), s);
   // factored: v[h] = o_lat[h] W_UV[h] (rounded to dtype), then y = v W_O
   void* vo = ws + W.vo;
-  st = run_gemm(W, G_OUT, W.g_ov, bf, true, o_lat, d->n_heads * d->d_latent, ab + L.uv, ws, base_epi(EPI_STORE_T, vo),
-                s);
+  st = run_gemm(W, G_OUT, W.g_ov, bf, !W.stage_o, a_op, d->n_heads * d->d_latent, ab + L.uv, ws,
+                base_epi(EPI_STORE_T, vo), s);
   if (st) return st;
   return run_gemm(W, G_OUT, W.g_oo, bf, false, vo, d->n_heads * d->d_v, ab + L.wo, ws, base_epi(EPI_F32, y), s);
 }

@@ -476,14 +476,101 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmArgs g) {
     }
   };
 
-  for (int s2 = 0; s2 < C::NSTAGE - 1; ++s2)
-    tiled_issue<C>(g, smem + s2 * C::STAGE, m0, nt0, kb0 + s2 * C::SKB, s2 < nst, wave, lane);
-  for (int s2 = 0; s2 < nst; ++s2) {
+  if constexpr (C::NSTAGE >= 4) {
+    // Pipelined ring: while the MFMAs of 16-k step q run, the fragments of
+    // step q + 1 are read from LDS into the registers step q + 1 used last
+    // time (after the last step of a stage: step 0 of the next stage), and
+    // the DMA of stage s + NSTAGE - 1 is spread over the MFMAs, so LDS
+    // reads overlap the matrix work.  Stage s + 1 has to be in LDS when
+    // stage s starts: NSTAGE - 3 stages stay in flight behind it.
+    constexpr int NQ = 2 * C::SKB;
+    constexpr int NMF = MTW * NTW;       // MFMAs per 16-k step
+    constexpr int NRD = MTW + NTW;       // fragment reads per 16-k step
+    bf16x8 af[NQ][MTW], bf[NQ][NTW];
+    auto read_one = [&](const unsigned char* __restrict__ st, int q, int u) __attribute__((always_inline)) {
+      const int kbl = q >> 1, k2 = q & 1;
+      if (u < MTW) {
+        const int rr = (wm * MTW + u) * 32 + a_row;
+        if constexpr (C::ESA == 2) {
+          const int c = (kbl * 4 + k2 * 2 + a_hi) ^ swz_a(rr, C::CPR);
+          af[q][u] = *reinterpret_cast<const bf16x8*>(st + a_off[u][0] + c * 16);
+        } else {
+          const int c0 = (kbl * 8 + k2 * 4 + a_hi * 2) ^ swz_a(rr, C::CPR);
+          const int c1 = (kbl * 8 + k2 * 4 + a_hi * 2 + 1) ^ swz_a(rr, C::CPR);
+          const float4 x0 = *reinterpret_cast<const float4*>(st + a_off[u][0] + c0 * 16);
+          const float4 x1 = *reinterpret_cast<const float4*>(st + a_off[u][0] + c1 * 16);
+          bf16x8 v;
+          v[0] = (__bf16)x0.x; v[1] = (__bf16)x0.y; v[2] = (__bf16)x0.z; v[3] = (__bf16)x0.w;
+          v[4] = (__bf16)x1.x; v[5] = (__bf16)x1.y; v[6] = (__bf16)x1.z; v[7] = (__bf16)x1.w;
+          af[q][u] = v;
+        }
+      } else {
+        const int j = u - MTW;
+        bf[q][j] = *reinterpret_cast<const bf16x8*>(st + b_off[j] + kbl * C::NTB * 1024 + k2 * 32 * 16);
+      }
+    };
+    // One stage: cur = its ring slot, nxt = the next stage's slot (read by
+    // the last step), dst = the slot the DMA fills; three distinct slots.
+    // (Every stage is whole: slices are a multiple of SKB k-blocks, checked
+    // at launch.  Reads are unconditional: a slot past the slice holds stale
+    // data that no MFMA uses.)
+    auto stage = [&](const unsigned char* __restrict__ cur, const unsigned char* __restrict__ nxt,
+                     unsigned char* __restrict__ dst, int kb_dma, bool dma_live) __attribute__((always_inline)) {
+      const TiledDma<C> dma = tiled_dma<C>(g, dst, m0, nt0, kb_dma, dma_live);
+      int issued = 0;
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        const bool last = q + 1 == NQ;
+        int rds = 0, mf = 0;
+#pragma unroll
+        for (int i = 0; i < MTW; ++i)
+#pragma unroll
+          for (int j = 0; j < NTW; ++j) {
+            // the step's reads over its first half of MFMAs
+            while (rds < NRD && 2 * mf * NRD >= rds * NMF) {
+              read_one(last ? nxt : cur, last ? 0 : q + 1, rds);
+              ++rds;
+            }
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[q][i], bf[q][j], acc[i][j], 0, 0, 0);
+            ++mf;
+            const int done = q * NMF + mf;
+            while (issued < C::LOADS && done * C::LOADS >= (issued + 1) * NQ * NMF) {
+              tiled_dma_one<C>(g, dma, issued, wave, lane);
+              ++issued;
+            }
+          }
+        while (rds < NRD) {
+          read_one(last ? nxt : cur, last ? 0 : q + 1, rds);
+          ++rds;
+        }
+      }
+    };
+    for (int s2 = 0; s2 < C::NSTAGE - 1; ++s2)
+      tiled_issue<C>(g, smem + s2 * C::STAGE, m0, nt0, kb0 + s2 * C::SKB, s2 < nst, wave, lane);
     vm_wait<(C::NSTAGE - 2) * C::LOADS>();
     lds_barrier();
-    const TiledDma<C> dma = tiled_dma<C>(g, smem + ((s2 + C::NSTAGE - 1) % C::NSTAGE) * C::STAGE, m0, nt0,
-                                         kb0 + (s2 + C::NSTAGE - 1) * C::SKB, s2 + C::NSTAGE - 1 < nst);
-    compute(smem + (s2 % C::NSTAGE) * C::STAGE, min(C::SKB, kb1 - kb0 - s2 * C::SKB), dma);
+#pragma unroll
+    for (int u = 0; u < NRD; ++u) read_one(smem, 0, u);
+    for (int s2 = 0; s2 < nst; ++s2) {
+      vm_wait<(C::NSTAGE - 3) * C::LOADS>();
+      lds_barrier();
+      unsigned char* cur = smem + (s2 % C::NSTAGE) * C::STAGE;
+      unsigned char* nxt = smem + ((s2 + 1) % C::NSTAGE) * C::STAGE;
+      unsigned char* dst = smem + ((s2 + C::NSTAGE - 1) % C::NSTAGE) * C::STAGE;
+      const int kb_dma = kb0 + (s2 + C::NSTAGE - 1) * C::SKB;
+      const bool dma_live = s2 + C::NSTAGE - 1 < nst;
+      stage(cur, nxt, dst, kb_dma, dma_live);
+    }
+  } else {
+    for (int s2 = 0; s2 < C::NSTAGE - 1; ++s2)
+      tiled_issue<C>(g, smem + s2 * C::STAGE, m0, nt0, kb0 + s2 * C::SKB, s2 < nst, wave, lane);
+    for (int s2 = 0; s2 < nst; ++s2) {
+      vm_wait<(C::NSTAGE - 2) * C::LOADS>();
+      lds_barrier();
+      const TiledDma<C> dma = tiled_dma<C>(g, smem + ((s2 + C::NSTAGE - 1) % C::NSTAGE) * C::STAGE, m0, nt0,
+                                           kb0 + (s2 + C::NSTAGE - 1) * C::SKB, s2 + C::NSTAGE - 1 < nst);
+      compute(smem + (s2 % C::NSTAGE) * C::STAGE, min(C::SKB, kb1 - kb0 - s2 * C::SKB), dma);
+    }
   }
   vm_wait<0>();
   lds_barrier();
@@ -755,7 +842,7 @@ GemmPlan plan_gemm(int M, int K, int N, bool bf16, bool a_f32, int n_cu, int a_g
       // sparse last round as much as a full one.  Each K slice adds an fp32
       // partial round trip.  A larger split must save 5% to be taken.
       const int lds = a_f32 ? (g.MT == 2 ? TiledCfg<float, 2, 2, 2>::LDS : TiledCfg<float, 1, 2, 2, 4>::LDS)
-                            : (g.MT == 2 ? TiledCfg<__bf16, 2, 2, 2>::LDS : TiledCfg<__bf16, 1, 2, 2>::LDS);
+                            : (g.MT == 2 ? TiledCfg<__bf16, 2, 2, 2, 4>::LDS : TiledCfg<__bf16, 1, 2, 2, 4>::LDS);
       const long slots = (long)n_cu * std::max(1, std::min(2, 160 * 1024 / lds));
       const double kb_bytes = BM * 32.0 * (a_f32 ? 4 : 2) + NTB * 1024.0;  // one block, one k-block
       double best_cost = 1e300;
@@ -803,6 +890,8 @@ static hipError_t launch_gemm_t(const GemmPlan& g, const GemmArgs& a, hipStream_
 template <typename TA, int MTW, int NTW, int SKB, int NS = 3, bool WNT = false>
 static hipError_t launch_tiled_t(const GemmPlan& g, const GemmArgs& a, hipStream_t s) {
   using C = TiledCfg<TA, MTW, NTW, SKB, NS, WNT>;
+  // the pipelined ring (four slots or more) runs whole stages only
+  if (NS >= 4 && (g.kblocks % SKB != 0 || g.kb_per_split % SKB != 0)) return hipErrorInvalidValue;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_tiled_kernel<TA, MTW, NTW, SKB, NS, WNT>),
@@ -820,17 +909,19 @@ static hipError_t launch_tiled_t(const GemmPlan& g, const GemmArgs& a, hipStream
 
 template <typename TA>
 static hipError_t launch_tiled_sel(const GemmPlan& g, const GemmArgs& a, hipStream_t s) {
-  if (g.MT == 4) return launch_tiled_t<TA, 4, 4, 1>(g, a, s);
-  // fp32 A doubles the bytes per stage: one block per CU, so a fourth
-  // stage keeps three in flight.  With bf16 A and one row block the
-  // weights are read once: non-temporal weight DMA (measured slower with
-  // the fp32-A kernel, so not used there)
+  // Four ring slots (the pipelined loop) wherever they fit in LDS: every
+  // bf16-A tile and the 64-row fp32-A tile; the larger fp32-A tiles keep
+  // three slots and the read-then-compute loop.
+  // With bf16 A and one row block the weights are read once: non-temporal
+  // weight DMA (measured slower with the fp32-A kernel, so not used there)
   if constexpr (sizeof(TA) == 4) {
+    if (g.MT == 4) return launch_tiled_t<TA, 4, 4, 1>(g, a, s);
     return g.MT == 2 ? launch_tiled_t<TA, 2, 2, 2>(g, a, s) : launch_tiled_t<TA, 1, 2, 2, 4>(g, a, s);
   } else {
+    if (g.MT == 4) return launch_tiled_t<TA, 4, 4, 1, 4>(g, a, s);
     if (g.gy == 1)
-      return g.MT == 2 ? launch_tiled_t<TA, 2, 2, 2, 3, true>(g, a, s) : launch_tiled_t<TA, 1, 2, 2, 3, true>(g, a, s);
-    return g.MT == 2 ? launch_tiled_t<TA, 2, 2, 2>(g, a, s) : launch_tiled_t<TA, 1, 2, 2>(g, a, s);
+      return g.MT == 2 ? launch_tiled_t<TA, 2, 2, 2, 4, true>(g, a, s) : launch_tiled_t<TA, 1, 2, 2, 4, true>(g, a, s);
+    return g.MT == 2 ? launch_tiled_t<TA, 2, 2, 2, 4>(g, a, s) : launch_tiled_t<TA, 1, 2, 2, 4>(g, a, s);
   }
 }
 
@@ -859,6 +950,28 @@ static hipError_t launch_gemm_sel(const GemmPlan& g, const GemmArgs& a, hipStrea
     return g.NT == 2 ? launch_gemm_t<T, TA, 4, 2, 4>(g, a, s) : launch_gemm_t<T, TA, 4, 4, 4>(g, a, s);
   }
   return launch_gemm_t<T, TA, 4, 4, 1>(g, a, s);
+}
+
+// fp32 -> bf16, rounded to nearest even: the rounding the fp32-A kernels
+// apply to each A fragment, so a GEMM over the converted copy is the same
+// computation.  8 values (32 B in, 16 B out) per thread and step.
+__global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float* __restrict__ x, __bf16* __restrict__ y, long n8) {
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n8; i += (long)gridDim.x * 256) {
+    const float4 u = reinterpret_cast<const float4*>(x)[2 * i], w = reinterpret_cast<const float4*>(x)[2 * i + 1];
+    bf16x8 v;
+    v[0] = (__bf16)u.x; v[1] = (__bf16)u.y; v[2] = (__bf16)u.z; v[3] = (__bf16)u.w;
+    v[4] = (__bf16)w.x; v[5] = (__bf16)w.y; v[6] = (__bf16)w.z; v[7] = (__bf16)w.w;
+    reinterpret_cast<bf16x8*>(y)[i] = v;
+  }
+}
+
+hipError_t launch_f32_to_bf16(const float* x, void* y, size_t n, hipStream_t s) {
+  if (n % 8 || (reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) % 16) return hipErrorInvalidValue;
+  if (n == 0) return hipSuccess;
+  const long n8 = (long)(n / 8);
+  const unsigned blocks = (unsigned)std::min<long>((n8 + 255) / 256, 4096L);
+  hipLaunchKernelGGL(f32_to_bf16_kernel, dim3(blocks), dim3(256), 0, s, x, reinterpret_cast<__bf16*>(y), n8);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm(const GemmPlan& g, bool bf16, bool a_f32, const void* A, int lda, const void* Wp, float* part,

@@ -64,6 +64,10 @@ struct GemmPlan {
 // tiled == -1 when no kernel configuration fits the groups.
 GemmPlan plan_gemm(int M, int K, int N, bool bf16, bool a_f32, int n_cu, int a_gtiles = 0, int a_gstride = 0);
 
+// fp32 -> bf16 copy (round to nearest even); n a multiple of 8, both
+// pointers 16-byte aligned.
+hipError_t launch_f32_to_bf16(const float* x, void* y, size_t n, hipStream_t s);
+
 // A is T (a_f32 == false) or fp32 (a_f32 == true); Wp is T.
 hipError_t launch_gemm(const GemmPlan& g, bool bf16, bool a_f32, const void* A, int lda, const void* Wp, float* part,
                        const EpiArgs& e, hipStream_t s);
