@@ -296,9 +296,11 @@ struct TiledCfg {
   static constexpr int NSTAGE = NSTAGE_;             // ring stages, NSTAGE - 1 in flight
   static constexpr int A_INST = A_BYTES / 1024, B_INST = SKB * NTB;
   static constexpr int LOADS = (A_INST + B_INST) / 4;  // DMA instructions per wave per stage
-  static constexpr int EPI_BYTES = BM / 2 * BN * 4;  // the epilogue stages half the block tile at a time
-  static constexpr int ROW_META = EPI_BYTES;          // then per-row positions / cache offsets (12 B per row)
-  static constexpr int EPI_TOTAL = EPI_BYTES + BM * 12;
+  // RoPE epilogue: half the block tile in fp32, rows padded by 16 bytes,
+  // then per-row positions / cache offsets (12 B per row)
+  static constexpr int TS = BN + 4;
+  static constexpr int ROW_META = BM / 2 * TS * 4;
+  static constexpr int EPI_TOTAL = ROW_META + BM * 12;
   static constexpr int LDS = NSTAGE * STAGE > EPI_TOTAL ? NSTAGE * STAGE : EPI_TOTAL;
   static_assert(A_INST % 4 == 0 && B_INST % 4 == 0, "whole DMA instructions per wave");
   static_assert(LDS <= 160 * 1024, "LDS budget");
@@ -465,7 +467,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmArgs g) {
       for (int i = 0; i < MTW; ++i)
 #pragma unroll
         for (int j = 0; j < NTW; ++j) {
-          if (q < nq) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[q][i], bf[q][j], acc[i][j], 0, 0, 0);
+          if (q < nq) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[q][j], af[q][i], acc[i][j], 0, 0, 0);
           ++mf;
           // DMA instruction u goes after MFMA (u + 1) * NMF / LOADS
           while (issued < C::LOADS && mf * C::LOADS >= (issued + 1) * NMF) {
@@ -531,7 +533,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmArgs g) {
               read_one(last ? nxt : cur, last ? 0 : q + 1, rds);
               ++rds;
             }
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[q][i], bf[q][j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[q][j], af[q][i], acc[i][j], 0, 0, 0);
             ++mf;
             const int done = q * NMF + mf;
             while (issued < C::LOADS && done * C::LOADS >= (issued + 1) * NQ * NMF) {
@@ -576,17 +578,25 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmArgs g) {
   lds_barrier();
 
   // ---- epilogue -----------------------------------------------------------
-  // Per-row values are looked up once per block and kept in LDS (a load per
-  // element pair would expose a memory round trip in every iteration): the
-  // token position (RoPE, cache slot) and, when appending, the element
-  // offset of the destination cache row (-1: no valid slot).  The block tile
-  // then goes through LDS one half of its rows at a time; each thread owns
-  // one column pair, so its RoPE frequency is set up once.
+  // The MFMAs take the weight fragment as their first operand, so the
+  // accumulators hold the transposed tile: lane l of tile (i, j) holds row
+  // (its row base) + l % 32 and, in registers 4u .. 4u + 3, the four
+  // consecutive columns 8u + 4 (l / 32) .. + 3 of the tile, written to LDS
+  // as one 16-byte store (rows padded by 16 bytes, so a wave's 32 rows fall
+  // in distinct banks).  The block tile goes through LDS one half of its
+  // rows at a time; each thread then owns one chunk of 8 consecutive
+  // columns, read back as 32 bytes and stored as 16 (bf16) or 32 (fp32)
+  // contiguous bytes, so a wave's store covers 1-2 KB of a row.
+  // Per-row values are looked up once per block into LDS (a load per row
+  // in the store loop would expose a memory round trip): the token position
+  // (RoPE) and, when appending, the element offset of the destination cache
+  // row (-1: no valid slot).
+  const EpiArgs& e = g.e;
   float* tile = reinterpret_cast<float*>(smem);
   int* row_pos = reinterpret_cast<int*>(smem + C::ROW_META);
   long long* row_dst = reinterpret_cast<long long*>(smem + C::ROW_META + C::BM * 4);
-  const EpiArgs& e = g.e;
-  const bool rope_mode = g.ksplit == 1 && (e.mode == EPI_Q || e.mode == EPI_APPEND);
+  const int mode = g.ksplit > 1 ? -1 : e.mode;  // -1: fp32 partial slice
+  const bool rope_mode = mode == EPI_Q || mode == EPI_APPEND;
   if (rope_mode) {
     for (int r = threadIdx.x; r < C::BM; r += 256) {
       const int m = m0 + r;
@@ -594,8 +604,8 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmArgs g) {
       long long dst = -1;
       if (m < e.M) {
         const int b = m / e.n_q, t = m - b * e.n_q;
-        pos = (e.mode == EPI_Q) ? e.kv_len[b] - e.n_q + t : e.pos[b] + t;
-        if (e.mode == EPI_APPEND) {
+        pos = (mode == EPI_Q) ? e.kv_len[b] - e.n_q + t : e.pos[b] + t;
+        if (mode == EPI_APPEND) {
           if (e.paged) {
             if (pos < 0 || pos >= e.max_pages * e.page_size) {
               atomicOr(e.err, 1);
@@ -617,28 +627,50 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmArgs g) {
       row_dst[r] = dst;
     }
   }
-  const int col0 = nt0 * 16;
   constexpr int HM = C::BM / 2;       // rows per half: the rows of the waves with wm == half
-  constexpr int CPB = C::BN / 2;      // column pairs per block row
-  constexpr int RSTEP = 256 / CPB;    // rows advanced per thread iteration
-  const int cp = threadIdx.x % CPB, r_first = threadIdx.x / CPB;
-  const int n = col0 + 2 * cp;
-  // column role: latent / rope pair j (rotation frequency in revolutions per position)
-  bool rope_col = false;
-  double rev_per_pos = 0.0;
-  const bool qm = e.mode == EPI_Q;
-  if (rope_mode && n < e.N) {
-    const int f = n % (qm ? e.qg_cols : e.row), rope0 = qm ? e.rope_from : e.d_latent;
-    if (f >= rope0) {
-      const int j = (f - rope0) >> 1;
-      rope_col = true;
-      rev_per_pos = exp2(-(2.0 * (double)j / (double)e.d_rope) * log2((double)e.rope_base)) * 0.15915494309189535;
+  constexpr int CPR = C::BN / 8;      // 8-column chunks per block row
+  constexpr int RSTEP = 256 / CPR;    // rows advanced per thread iteration
+  const int cc = threadIdx.x % CPR, r_first = threadIdx.x / CPR;
+  const int n = nt0 * 16 + 8 * cc;    // first column of this thread's chunk
+  const bool qm = mode == EPI_Q;
+  // Per column pair p of the chunk (rope modes): rotation frequency in
+  // revolutions per position (0: not a rope column) and the destination
+  // column (EPI_Q maps the column through its groups)
+  double rev[4] = {0.0, 0.0, 0.0, 0.0};
+  size_t dcol[4] = {0, 0, 0, 0};
+  bool q_contig = false;  // the 8 destination columns are consecutive (EPI_Q)
+  if (rope_mode) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int nn = n + 2 * p;
+      if (nn >= e.N) break;
+      const int f = nn % (qm ? e.qg_cols : e.row), rope0 = qm ? e.rope_from : e.d_latent;
+      if (f >= rope0)
+        rev[p] = exp2(-(2.0 * (double)((f - rope0) >> 1) / (double)e.d_rope) * log2((double)e.rope_base)) *
+                 0.15915494309189535;
+      dcol[p] = qm ? (size_t)e.q_off + (size_t)(nn / e.qg_cols) * e.qg_stride + f : (size_t)nn;
     }
+    q_contig = qm && n + 7 < e.N && n / e.qg_cols == (n + 7) / e.qg_cols;
   }
-  // bf16 destination of this thread's column pair: row stride and column
-  // offset (EPI_Q maps the column through its groups)
-  const size_t q_ld = qm ? (size_t)e.q_ld : (size_t)e.N;
-  const size_t q_col = (qm && n < e.N) ? (size_t)e.q_off + (size_t)(n / e.qg_cols) * e.qg_stride + n % e.qg_cols : (size_t)n;
+  // (angle reduced to (-1/2, 1/2] revolutions in fp64, then the hardware
+  // sine / cosine, whose argument is in revolutions)
+  auto rotate = [&](int pos, double rv, float& x, float& y) {
+    double a = (double)pos * rv;
+    a -= rint(a);
+    const float rf = (float)a;
+    const float c = __builtin_amdgcn_cosf(rf), sn = __builtin_amdgcn_sinf(rf);
+    const float a0 = x, a1 = y;
+    x = a0 * c - a1 * sn;
+    y = a0 * sn + a1 * c;
+  };
+  auto bf2 = [](float x, float y) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 t = {(__bf16)x, (__bf16)y};
+    return __builtin_bit_cast(uint32_t, t);
+  };
+  const int nlim = mode == -1 ? g.Np : e.N;  // columns that exist in the destination
+  const int ldo = mode == -1 ? g.Np : e.N;   // its row stride (fp32 / bf16 plain outputs)
+  const bool whole = n + 7 < nlim;           // all 8 columns of the chunk exist
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     if (wm == half) {
@@ -647,85 +679,71 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < NTW; ++j)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = i * 32 + 8 * (r >> 2) + 4 * a_hi + (r & 3);
-            const int col = (wn * NTW + j) * 32 + (lane & 31);
-            tile[row * C::BN + col] = acc[i][j][r];
+          for (int u = 0; u < 4; ++u) {
+            const int row = i * 32 + a_row;
+            const int col = (wn * NTW + j) * 32 + 8 * u + 4 * a_hi;
+            *reinterpret_cast<float4*>(tile + row * C::TS + col) =
+                make_float4(acc[i][j][4 * u], acc[i][j][4 * u + 1], acc[i][j][4 * u + 2], acc[i][j][4 * u + 3]);
           }
     }
     __syncthreads();
-    // rows r_first + RSTEP u: UR rows per batch, their LDS reads issued
-    // together; the mode is uniform, so each mode has its own loop
-    constexpr int UR = 8;
     const int mlim = e.M - (m0 + half * HM);  // rows of this half that exist
-    auto rows = [&](auto body) {
-      for (int r0 = r_first; r0 < HM; r0 += UR * RSTEP) {
-        float2 v[UR];
-#pragma unroll
-        for (int u = 0; u < UR; ++u) {
-          const int r = r0 + u * RSTEP;
-          v[u] = r < HM ? *reinterpret_cast<const float2*>(tile + r * C::BN + 2 * cp) : make_float2(0.f, 0.f);
-        }
-#pragma unroll
-        for (int u = 0; u < UR; ++u) {
-          const int r = r0 + u * RSTEP;
-          if (r < HM && r < mlim) body(r, v[u]);
-        }
-      }
-    };
-    if (n < g.Np) {
-      if (g.ksplit > 1) {
-        rows([&](int r, float2 v) {
-          *reinterpret_cast<float2*>(g.part + ((size_t)ks * e.M + m0 + half * HM + r) * g.Np + n) = v;
-        });
-      } else if (n < e.N) {
-        const bool has1 = n + 1 < e.N;
-        if (e.mode == EPI_F32) {
-          rows([&](int r, float2 v) {
-            float* y = reinterpret_cast<float*>(e.out) + (size_t)(m0 + half * HM + r) * e.N + n;
-            if (has1)
-              *reinterpret_cast<float2*>(y) = v;
-            else
-              y[0] = v.x;
-          });
-        } else {
-          // bf16 pair store; RoPE rotation for rope columns (angle reduced to
-          // (-1/2, 1/2] revolutions in fp64, then the hardware sine / cosine,
-          // whose argument is in revolutions)
-          auto store = [&](__bf16* y, float v0, float v1) {
-            if (has1) {
-              __bf16 pr[2] = {(__bf16)v0, (__bf16)v1};
-              *reinterpret_cast<uint32_t*>(y) = *reinterpret_cast<const uint32_t*>(pr);
-            } else {
-              y[0] = (__bf16)v0;
-            }
-          };
-          auto rotate = [&](int rb, float2& v) {
-            double rev = (double)row_pos[rb] * rev_per_pos;
-            rev -= rint(rev);
-            const float rf = (float)rev;
-            const float c = __builtin_amdgcn_cosf(rf), sn = __builtin_amdgcn_sinf(rf);
-            const float a0 = v.x, a1 = v.y;
-            v.x = a0 * c - a1 * sn;
-            v.y = a0 * sn + a1 * c;
-          };
-          if (e.mode == EPI_APPEND) {
-            rows([&](int r, float2 v) {
-              const int rb = half * HM + r;
-              const long long d = row_dst[rb];
-              if (rope_col) rotate(rb, v);
-              if (d >= 0) store(reinterpret_cast<__bf16*>(e.pool) + d + n, v.x, v.y);
-            });
-          } else if (rope_col) {
-            rows([&](int r, float2 v) {
-              const int rb = half * HM + r;
-              rotate(rb, v);
-              store(reinterpret_cast<__bf16*>(e.out) + (size_t)(m0 + rb) * q_ld + q_col, v.x, v.y);
-            });
+    if (n < nlim) {
+      for (int r = r_first; r < HM && r < mlim; r += RSTEP) {
+        const float4 lo = *reinterpret_cast<const float4*>(tile + r * C::TS + 8 * cc);
+        const float4 hi = *reinterpret_cast<const float4*>(tile + r * C::TS + 8 * cc + 4);
+        float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        const int rb = half * HM + r;
+        const size_t m = (size_t)(m0 + rb);
+        if (mode == -1 || mode == EPI_F32) {
+          float* y = (mode == -1 ? g.part + (size_t)ks * e.M * g.Np : reinterpret_cast<float*>(e.out)) + m * ldo + n;
+          if (whole && (ldo & 3) == 0) {
+            reinterpret_cast<float4*>(y)[0] = lo;
+            reinterpret_cast<float4*>(y)[1] = hi;
           } else {
-            rows([&](int r, float2 v) {
-              store(reinterpret_cast<__bf16*>(e.out) + (size_t)(m0 + half * HM + r) * q_ld + q_col, v.x, v.y);
-            });
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+              if (n + c < nlim) y[c] = v[c];
+          }
+        } else if (mode == EPI_STORE_T) {
+          __bf16* y = reinterpret_cast<__bf16*>(e.out) + m * ldo + n;
+          if (whole && (ldo & 7) == 0) {
+            *reinterpret_cast<uint4*>(y) = make_uint4(bf2(v[0], v[1]), bf2(v[2], v[3]), bf2(v[4], v[5]), bf2(v[6], v[7]));
+          } else {
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+              if (n + c < nlim) y[c] = (__bf16)v[c];
+          }
+        } else {
+          // EPI_Q / EPI_APPEND: rotate the rope pairs, then one 16-byte
+          // store when the 8 destination columns are consecutive and
+          // aligned, else a store per pair
+          const int pos = row_pos[rb];
+          __bf16* base;
+          if (qm) {
+            base = reinterpret_cast<__bf16*>(e.out) + m * e.q_ld;
+          } else {
+            const long long d = row_dst[rb];
+            if (d < 0) continue;
+            base = reinterpret_cast<__bf16*>(e.pool) + d;
+          }
+#pragma unroll
+          for (int p = 0; p < 4; ++p)
+            if (rev[p] != 0.0) rotate(pos, rev[p], v[2 * p], v[2 * p + 1]);
+          const bool contig = qm ? q_contig : whole;
+          if (contig && ((reinterpret_cast<uintptr_t>(base + dcol[0])) & 15) == 0) {
+            *reinterpret_cast<uint4*>(base + dcol[0]) =
+                make_uint4(bf2(v[0], v[1]), bf2(v[2], v[3]), bf2(v[4], v[5]), bf2(v[6], v[7]));
+          } else {
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+              const int nn = n + 2 * p;
+              if (nn >= e.N) break;
+              if (nn + 1 < e.N)
+                *reinterpret_cast<uint32_t*>(base + dcol[p]) = bf2(v[2 * p], v[2 * p + 1]);
+              else
+                base[dcol[p]] = (__bf16)v[2 * p];
+            }
           }
         }
       }
