@@ -90,16 +90,17 @@ def counters_per_dispatch(path):
     return out
 
 
-def last_step(per_dispatch):
-    """The dispatches of the last bench step, each mapped to its call.
+def steps(per_dispatch):
+    """The bench steps in the dispatch list, each a list of (call, dispatch id).
 
     A step is: the append GEMM, the two q-projection GEMMs, the attention
-    plan / split / merge kernels, the output GEMM; a GEMM whose K range is
-    split is followed by its epilogue kernel.  The step is anchored at its
-    attention plan kernel."""
+    plan / split / merge kernels, then the output projection (its GEMM,
+    preceded by the fp32 -> bf16 staging of o_lat when the large tiling
+    takes it); a GEMM whose K range is split is followed by its epilogue
+    kernel.  Steps are anchored at their attention plan kernels."""
     ids = [d for d in sorted(per_dispatch) if mla_kernel(per_dispatch[d][0])]
     names = [per_dispatch[d][0] for d in ids]
-    plan = max(i for i, n in enumerate(names) if "attn_plan" in n)
+    plans = [i for i, n in enumerate(names) if "attn_plan" in n]
 
     def gemm_groups_before(end, count):
         groups, i = [], end - 1
@@ -112,14 +113,42 @@ def last_step(per_dispatch):
             i -= 1
         return groups
 
-    pre = gemm_groups_before(plan, 3)
-    calls = [("mla_compress_append", i) for i in pre[0]] + [("mla_q_proj", i) for g in pre[1:] for i in g]
-    calls += [("mla_attention", plan), ("mla_attention", plan + 1), ("mla_attention", plan + 2)]
-    i = plan + 3
-    calls.append(("mla_out_proj", i))
-    if i + 1 < len(names) and "splitk_epilogue" in names[i + 1]:
-        calls.append(("mla_out_proj", i + 1))
-    return [(c, names[i], per_dispatch[ids[i]][1]) for c, i in calls]
+    out = []
+    for plan in plans:
+        if plan < 3:
+            continue
+        pre = gemm_groups_before(plan, 3)
+        calls = [("mla_compress_append", i) for i in pre[0]] + [("mla_q_proj", i) for g in pre[1:] for i in g]
+        calls += [("mla_attention", plan), ("mla_attention", plan + 1), ("mla_attention", plan + 2)]
+        i = plan + 3
+        if i < len(names) and "f32_to_bf16" in names[i]:
+            calls.append(("mla_out_proj", i))
+            i += 1
+        if i < len(names):
+            calls.append(("mla_out_proj", i))
+            if i + 1 < len(names) and "splitk_epilogue" in names[i + 1]:
+                calls.append(("mla_out_proj", i + 1))
+        out.append([(c, ids[k]) for c, k in calls])
+    return out
+
+
+def last_step(per_dispatch):
+    """(call, kernel name, value) for the dispatches of the last bench step."""
+    return [(c, per_dispatch[d][0], per_dispatch[d][1]) for c, d in steps(per_dispatch)[-1]]
+
+
+def trace_durations(path, skip=5):
+    """Per position of a step: mean duration (us) over the traced steps after
+    the first `skip` (warm-up), from a kernel-trace CSV."""
+    per = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            d = int(r["Dispatch_Id"])
+            per[d] = (r["Kernel_Name"], (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    st = steps(per)[skip:]
+    n = len(st[-1])
+    st = [s for s in st if len(s) == n]
+    return [sum(per[s[k][1]][1] for s in st) / len(st) for k in range(n)]
 
 
 def main():
@@ -189,17 +218,21 @@ def main():
     stats = find(args.out, "trace", "kernel_stats.csv")
     with open(stats) as f:
         krows = sorted(csv.DictReader(f), key=lambda r: -float(r["TotalDurationNs"]))
-    avg_us = {r["Name"]: float(r["AverageNs"]) / 1e3 for r in krows}
+    # mean duration of each position of a step over the traced steps (one
+    # kernel can serve several calls, so durations go by position, not name)
+    pos_us = trace_durations(find(args.out, "trace", "kernel_trace.csv"))
 
     # MFMA per dispatch of the last step: counted flops, busy fraction, and
-    # the rate over the kernel's average duration in the trace pass
+    # the rate over that position's mean duration in the trace pass
     mrows, mcalls = [], {c: {"flops": 0.0, "us": 0.0, "busy": 0.0, "active": 0.0} for c in CALLS}
     mf_step = last_step({d: (n, d) for d, (n, _) in mf.items()})
-    for call, name, d in mf_step:
+    if len(mf_step) != len(pos_us):
+        raise SystemExit(f"step shapes differ: {len(mf_step)} counted dispatches, {len(pos_us)} traced")
+    for k, (call, name, d) in enumerate(mf_step):
         v = mf[int(d)][1]
         flops = v.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * flops_per_mop
         busy, active = v.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0), v.get("GRBM_GUI_ACTIVE", 0.0) / N_XCD
-        us = avg_us.get(name, float("nan"))
+        us = pos_us[k]
         mrows.append((call, name, flops, busy / (active * N_SIMD) if active else 0.0, us))
         m = mcalls[call]
         m["flops"] += flops
@@ -238,7 +271,7 @@ def main():
                 f" ; {flops_per_mop:.1f} flops per counted operation (2 n^3 over the product's counter)\n")
         f.write(f"# busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {N_XCD} XCDs x {N_SIMD} SIMDs); "
                 f"rate = counted flops / "
-                f"the kernel's average duration in the kernel-trace run; peak 2500 TFLOP/s (dense bf16)\n")
+                f"that dispatch's mean duration over the steps of the kernel-trace run; peak 2500 TFLOP/s (dense bf16)\n")
         f.write(f"{'call':22s} {'kernel':70s} {'GFLOP':>10s} {'avg_us':>9s} {'TFLOP/s':>9s} {'%peak':>7s} {'busy%':>7s}\n")
         for call, name, fl, bz, us in mrows:
             f.write(f"{call:22s} {name[:70]:70s} {fl / 1e9:10.3f} {us:9.2f} {fl / (us * 1e-6) / 1e12:9.1f} "
