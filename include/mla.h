@@ -227,7 +227,10 @@ mla_status mla_decode(const mla_dims *dims, const void *absorbed, const void *x,
  * "Two merges", output side): y[n] = sum_h o_lat[n][h] W_UVO[h]; in the
  * factored form v[h] = o_lat[n][h] W_UV[h] (rounded to dtype), then
  * y[n] = sum_h v[h] W_O[h].
- *   o_lat [n_tok, H, d_latent] fp32;  y [n_tok, d_model] fp32 out. */
+ *   o_lat [n_tok, H, d_latent] fp32;  y [n_tok, d_model] fp32 out.
+ * For a bf16 layer with enough rows (the 256-row tiling), o_lat is first
+ * rounded to bf16 into the workspace (the rounding every bf16 product
+ * applies to it anyway); mla_workspace_size counts that region. */
 mla_status mla_out_proj(const mla_dims *dims, const void *absorbed, const float *o_lat, int32_t n_tok, float *y,
                         void *workspace, size_t ws_bytes, void *stream);
 
