@@ -145,17 +145,20 @@ struct WsLayout {
   GemmPlan g_qn, g_qr, g_qk, g_ov, g_oo;
   int G, V;
   bool plans_ok;
-  // o_lat goes through a bf16 copy (ob) before the output projection: set
-  // when the fp32-A plan would be the 256 x 256 tiling, whose fp32 stages
-  // leave LDS room for three ring slots only; the bf16-A plan replaces it
+  // o_lat goes through a bf16 copy (ob) before the merged output
+  // projection when that runs LDS-tiled: every column block re-reads the
+  // whole A operand (at 64 rows as many bytes as the weights), which the
+  // bf16 copy halves, and the 256 x 256 fp32-A tiling leaves LDS room for
+  // three ring slots only.  (The factored form's per-head products read
+  // each head's A columns in one block: nothing to save there.)
   bool stage_o;
 };
 
 // The fp32-A plan, or the bf16-A plan over a staged copy (stage_o) when the
-// fp32 one is the 256 x 256 tiling.
+// fp32 one is LDS-tiled and A has no column groups.
 static GemmPlan plan_o(bool bf, int M, int K, int N, int ncu, int gt, int gs, bool* staged) {
   GemmPlan g = plan_gemm(M, K, N, bf, true, ncu, gt, gs);
-  if (bf && g.tiled == 1 && g.MT == 4) {
+  if (bf && g.tiled == 1 && gt == 0) {
     const GemmPlan b = plan_gemm(M, K, N, bf, false, ncu, gt, gs);
     if (b.tiled == 1) {
       *staged = true;
