@@ -281,6 +281,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
 // large-M configuration uses 128 x 128 wave tiles (0.5 KB per MFMA) to stay
 // clear of the LDS bandwidth.
 // --------------------------------------------------------------------------
+// An unsplit K of at most this many k-blocks counts as short (ring choice)
+constexpr int kShortSlice = 64;
+
 template <typename TA, int MTW, int NTW, int SKB_, int NSTAGE_ = 3, bool WNT_ = false>
 struct TiledCfg {
   static constexpr bool WNT = WNT_;                  // weights read once: non-temporal DMA
@@ -937,8 +940,16 @@ static hipError_t launch_tiled_sel(const GemmPlan& g, const GemmArgs& a, hipStre
     return g.MT == 2 ? launch_tiled_t<TA, 2, 2, 2>(g, a, s) : launch_tiled_t<TA, 1, 2, 2, 4>(g, a, s);
   } else {
     if (g.MT == 4) return launch_tiled_t<TA, 4, 4, 1, 4>(g, a, s);
-    if (g.gy == 1)
+    // 64-row blocks over an unsplit short K: the 3-slot ring, which fits
+    // two blocks per CU (the fill and the epilogue of one hide under the
+    // other; measured better for a 1536-deep query projection, worse for
+    // the long output-projection slices)
+    const bool short_slice = g.MT == 1 && g.ksplit == 1 && g.kb_per_split <= kShortSlice;
+    if (g.gy == 1) {
+      if (short_slice) return launch_tiled_t<TA, 1, 2, 2, 3, true>(g, a, s);
       return g.MT == 2 ? launch_tiled_t<TA, 2, 2, 2, 4, true>(g, a, s) : launch_tiled_t<TA, 1, 2, 2, 4, true>(g, a, s);
+    }
+    if (short_slice) return launch_tiled_t<TA, 1, 2, 2, 3>(g, a, s);
     return g.MT == 2 ? launch_tiled_t<TA, 2, 2, 2, 4>(g, a, s) : launch_tiled_t<TA, 1, 2, 2, 4>(g, a, s);
   }
 }
