@@ -902,13 +902,7 @@ size_t attn_sched_ints(int U, int G) { return 6 * (size_t)U + 8 * (size_t)G; }
 
 template <class C>
 static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t s) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_split_kernel<C>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  if (hipError_t e = ensure_lds_limit<&attn_split_kernel<C>>(C::LDS_BYTES); e != hipSuccess) return e;
   const int cap = a.paged ? a.max_pages * a.page_size : a.s_max;
   hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, a, cap);
   hipError_t e = hipGetLastError();
@@ -1180,13 +1174,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillArgs a) {
 }
 
 hipError_t launch_prefill_attention(const PrefillArgs& a, hipStream_t s) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_attn_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kFaLds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  if (hipError_t e = ensure_lds_limit<&prefill_attn_kernel>(kFaLds); e != hipSuccess) return e;
   hipLaunchKernelGGL(prefill_attn_kernel, dim3((a.n_q + 127) / 128, a.H, a.B), dim3(256), kFaLds, s, a);
   return hipGetLastError();
 }

@@ -11,6 +11,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -114,4 +116,21 @@ __device__ inline void rope_cos_sin(int pos, int j, int d_rope, float base, floa
   sincos((double)pos * theta, &sd, &cd);
   *c = (float)cd;
   *s = (float)sd;
+}
+
+// Raises kernel K's dynamic LDS limit to `bytes` on the current device, once
+// per device (the attribute is per device; setting it twice is harmless, so
+// concurrent first calls only repeat it).  Devices beyond 64 set it on every
+// call.
+template <auto K>
+inline hipError_t ensure_lds_limit(int bytes) {
+  static std::atomic<uint64_t> done{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? (uint64_t{1} << dev) : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(K), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+  return e;
 }

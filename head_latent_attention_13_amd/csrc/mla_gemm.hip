@@ -913,13 +913,8 @@ static hipError_t launch_tiled_t(const GemmPlan& g, const GemmArgs& a, hipStream
   using C = TiledCfg<TA, MTW, NTW, SKB, NS, WNT>;
   // the pipelined ring (four slots or more) runs whole stages only
   if (NS >= 4 && (g.kblocks % SKB != 0 || g.kb_per_split % SKB != 0)) return hipErrorInvalidValue;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_tiled_kernel<TA, MTW, NTW, SKB, NS, WNT>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  if (hipError_t e = ensure_lds_limit<&gemm_tiled_kernel<TA, MTW, NTW, SKB, NS, WNT>>(C::LDS); e != hipSuccess)
+    return e;
   hipLaunchKernelGGL((gemm_tiled_kernel<TA, MTW, NTW, SKB, NS, WNT>), dim3(g.gy, g.gx, g.ksplit), dim3(256), C::LDS, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || g.ksplit == 1) return e;
