@@ -44,6 +44,8 @@ def parse():
     p.add_argument("--prefill", choices=("absorbed", "expanded"), default="absorbed",
                    help="expanded: the step is append + mla_prefill_expanded (factored weights, contiguous cache; "
                         "the V3 chunked-prefill workload)")
+    p.add_argument("--graph", action="store_true",
+                   help="replay each step from a HIP graph captured once per input copy")
     p.add_argument("--copies", type=int, default=4,
                    help="input sets (absorbed weights, cache, activations) rotated over the steps, so that no "
                         "step finds its inputs in the 256 MB last-level cache")
@@ -279,12 +281,30 @@ def main():
     for k in range(args.warmup):
         step(k)
     torch.cuda.synchronize()
+    run = step
+    if args.graph:
+        # one graph per input copy, captured after the warm-up (the library
+        # allocates nothing and issues no memset, so a step captures whole)
+        graphs = []
+        for j in range(NC):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(j)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+        def run(k):
+            graphs[k % NC].replay()
+
+        for k in range(args.warmup):
+            run(k)
+        torch.cuda.synchronize()
     # timed region: K whole steps back to back, events only at its ends
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     t_start.record()
     for k in range(args.steps):
-        step(k)
+        run(k)
     t_end.record()
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
@@ -379,7 +399,8 @@ def main():
                                                                       else int(cfg.cached)),
                    "new_tokens": n_q, "heads": H, "d_latent": cfg.d_latent, "d_rope": cfg.d_rope,
                    "d_model": cfg.d_model, "cache": "paged" if cfg.paged else "contiguous",
-                   "weights": args.form, "prefill": args.prefill},
+                   "weights": args.form, "prefill": args.prefill,
+                   "launch": "HIP graph per step" if args.graph else "stream"},
         "roofline": roofline,
         "latent_cache_GB_s": round(cache_bytes / (per_call_ms["mla_prefill_expanded" if expanded else "mla_attention"]
                                                    * 1e-3) / 1e9, 1),
