@@ -156,10 +156,10 @@ struct WsLayout {
 
 // The fp32-A plan, or the bf16-A plan over a staged copy (stage_o) when the
 // fp32 one is LDS-tiled and A has no column groups.
-static GemmPlan plan_o(bool bf, int M, int K, int N, int ncu, int gt, int gs, bool* staged) {
-  GemmPlan g = plan_gemm(M, K, N, bf, true, ncu, gt, gs);
+static GemmPlan plan_o(bool bf, int M, int K, int N, int ncu, int gt, int gs, bool* staged, size_t cap) {
+  GemmPlan g = plan_gemm(M, K, N, bf, true, ncu, gt, gs, cap);
   if (bf && g.tiled == 1 && gt == 0) {
-    const GemmPlan b = plan_gemm(M, K, N, bf, false, ncu, gt, gs);
+    const GemmPlan b = plan_gemm(M, K, N, bf, false, ncu, gt, gs, cap);
     if (b.tiled == 1) {
       *staged = true;
       return b;
@@ -168,26 +168,27 @@ static GemmPlan plan_o(bool bf, int M, int K, int N, int ncu, int gt, int gs, bo
   return g;
 }
 
-WsLayout ws_layout(const mla_dims* d, int batch, int n_q) {
+// cap: the most bytes the GEMMs' split-K partials may take (ws_fit).
+WsLayout ws_layout(const mla_dims* d, int batch, int n_q, size_t cap = SIZE_MAX) {
   WsLayout W{};
   const bool bf = is_bf16(d);
   const int M = batch * n_q, R = row_width(d), H = d->n_heads;
   const int ncu = device_cus();
-  W.g_app = plan_gemm(M, d->d_model, R, bf, false, ncu);
-  W.g_cq = plan_gemm(M, d->d_model, d->d_q_latent, bf, false, ncu);
+  W.g_app = plan_gemm(M, d->d_model, R, bf, false, ncu, 0, 0, cap);
+  W.g_cq = plan_gemm(M, d->d_model, d->d_q_latent, bf, false, ncu, 0, 0, cap);
   size_t part = std::max(W.g_app.part_bytes, W.g_cq.part_bytes);
   if (!factored(d)) {
-    W.g_q = plan_gemm(M, d->d_q_latent, H * R, bf, false, ncu);
-    W.g_out = plan_o(bf, M, H * d->d_latent, d->d_model, ncu, 0, 0, &W.stage_o);
+    W.g_q = plan_gemm(M, d->d_q_latent, H * R, bf, false, ncu, 0, 0, cap);
+    W.g_out = plan_o(bf, M, H * d->d_latent, d->d_model, ncu, 0, 0, &W.stage_o, cap);
     part = std::max(part, std::max(W.g_q.part_bytes, W.g_out.part_bytes));
     W.plans_ok = true;
   } else {
-    W.g_qn = plan_gemm(M, d->d_q_latent, H * d->d_nope, bf, false, ncu);
-    W.g_qr = plan_gemm(M, d->d_q_latent, H * d->d_rope, bf, false, ncu);
+    W.g_qn = plan_gemm(M, d->d_q_latent, H * d->d_nope, bf, false, ncu, 0, 0, cap);
+    W.g_qr = plan_gemm(M, d->d_q_latent, H * d->d_rope, bf, false, ncu, 0, 0, cap);
     // per-head products: head h's output tiles read A columns h*K ..
-    W.g_qk = plan_gemm(M, d->d_nope, H * d->d_latent, bf, false, ncu, d->d_latent / 16, d->d_nope);
-    W.g_ov = plan_o(bf, M, d->d_latent, H * d->d_v, ncu, d->d_v / 16, d->d_latent, &W.stage_o);
-    W.g_oo = plan_gemm(M, H * d->d_v, d->d_model, bf, false, ncu);
+    W.g_qk = plan_gemm(M, d->d_nope, H * d->d_latent, bf, false, ncu, d->d_latent / 16, d->d_nope, cap);
+    W.g_ov = plan_o(bf, M, d->d_latent, H * d->d_v, ncu, d->d_v / 16, d->d_latent, &W.stage_o, cap);
+    W.g_oo = plan_gemm(M, H * d->d_v, d->d_model, bf, false, ncu, 0, 0, cap);
     for (const GemmPlan* g : {&W.g_qn, &W.g_qr, &W.g_qk, &W.g_ov, &W.g_oo}) part = std::max(part, g->part_bytes);
     W.plans_ok = W.g_qk.tiled >= 0 && W.g_ov.tiled >= 0;
   }
@@ -213,6 +214,19 @@ WsLayout ws_layout(const mla_dims* d, int batch, int n_q) {
   W.attn_o = o; o = align256(o + slots * HG * d->d_latent * 4);
   W.attn_lse = o; o = align256(o + slots * HG * 4);
   W.total = o;
+  return W;
+}
+
+// The layout of a call on a workspace of ws_bytes: that of ws_layout or,
+// when its split-K partials do not fit, the plans whose partials fit the
+// bytes the other regions leave (an unsplit plan needs none).  Every other
+// region grows with the row count, so a workspace sized by
+// mla_workspace_size for (batch, n_q) serves every call with fewer rows,
+// although the K splits that fit best differ from one row count to another.
+WsLayout ws_fit(const mla_dims* d, int batch, int n_q, size_t ws_bytes) {
+  WsLayout W = ws_layout(d, batch, n_q);
+  const size_t rest = W.total - (W.tile_off - W.part);  // all but the partial region
+  if (W.total > ws_bytes && ws_bytes > rest) W = ws_layout(d, batch, n_q, (ws_bytes - rest) & ~(size_t)255);
   return W;
 }
 
@@ -336,16 +350,16 @@ struct PfLayout {
   bool plans_ok;
 };
 
-PfLayout pf_layout(const mla_dims* d, int batch, int n_q, int s_max) {
+PfLayout pf_layout(const mla_dims* d, int batch, int n_q, int s_max, size_t cap = SIZE_MAX) {
   PfLayout P{};
   const int M = batch * n_q, Mk = batch * s_max, H = d->n_heads, ncu = device_cus();
   const int QE = d->d_nope + d->d_rope;
-  P.g_cq = plan_gemm(M, d->d_model, d->d_q_latent, true, false, ncu);
-  P.g_qn = plan_gemm(M, d->d_q_latent, H * d->d_nope, true, false, ncu);
-  P.g_qr = plan_gemm(M, d->d_q_latent, H * d->d_rope, true, false, ncu);
-  P.g_k = plan_gemm(Mk, d->d_latent, H * d->d_nope, true, false, ncu);
-  P.g_v = plan_gemm(Mk, d->d_latent, H * d->d_v, true, false, ncu);
-  P.g_oo = plan_gemm(M, H * d->d_v, d->d_model, true, false, ncu);
+  P.g_cq = plan_gemm(M, d->d_model, d->d_q_latent, true, false, ncu, 0, 0, cap);
+  P.g_qn = plan_gemm(M, d->d_q_latent, H * d->d_nope, true, false, ncu, 0, 0, cap);
+  P.g_qr = plan_gemm(M, d->d_q_latent, H * d->d_rope, true, false, ncu, 0, 0, cap);
+  P.g_k = plan_gemm(Mk, d->d_latent, H * d->d_nope, true, false, ncu, 0, 0, cap);
+  P.g_v = plan_gemm(Mk, d->d_latent, H * d->d_v, true, false, ncu, 0, 0, cap);
+  P.g_oo = plan_gemm(M, H * d->d_v, d->d_model, true, false, ncu, 0, 0, cap);
   size_t part = 0;
   for (const GemmPlan* g : {&P.g_cq, &P.g_qn, &P.g_qr, &P.g_k, &P.g_v, &P.g_oo}) part = std::max(part, g->part_bytes);
   P.plans_ok = true;
@@ -358,6 +372,13 @@ PfLayout pf_layout(const mla_dims* d, int batch, int n_q, int s_max) {
   P.vo = o; o = align256(o + (size_t)M * H * d->d_v * 2);
   P.part = o; o = align256(o + part);
   P.total = o;
+  return P;
+}
+
+// As ws_fit, for the expanded prefill (the partial region comes last).
+PfLayout pf_fit(const mla_dims* d, int batch, int n_q, int s_max, size_t ws_bytes) {
+  PfLayout P = pf_layout(d, batch, n_q, s_max);
+  if (P.total > ws_bytes && ws_bytes > P.part) P = pf_layout(d, batch, n_q, s_max, (ws_bytes - P.part) & ~(size_t)255);
   return P;
 }
 
@@ -459,7 +480,7 @@ mla_status mla_compress_append(const mla_dims* d, const void* absorbed, const vo
   if (!absorbed || !x || !pos) return fail(MLA_ERR_INVALID_ARG, "absorbed, x and pos must be non-NULL");
   if (!aligned(x, 16)) return fail(MLA_ERR_INVALID_ARG, "x must be 16-byte aligned");
   if ((st = check_cache(d, cache, batch))) return st;
-  const WsLayout W = ws_layout(d, batch, n_q);
+  const WsLayout W = ws_fit(d, batch, n_q, ws_bytes);
   if ((st = check_ws(W, workspace, ws_bytes))) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool bf = is_bf16(d);
@@ -482,7 +503,7 @@ mla_status mla_q_proj(const mla_dims* d, const void* absorbed, const void* x, co
   if (st) return st;
   if (!absorbed || !x || !kv_len || !q) return fail(MLA_ERR_INVALID_ARG, "absorbed, x, kv_len and q must be non-NULL");
   if (!aligned(x, 16) || !aligned(q, 16)) return fail(MLA_ERR_INVALID_ARG, "x and q must be 16-byte aligned");
-  const WsLayout W = ws_layout(d, batch, n_q);
+  const WsLayout W = ws_fit(d, batch, n_q, ws_bytes);
   if ((st = check_ws(W, workspace, ws_bytes))) return st;
   return q_proj_impl(d, W, reinterpret_cast<const unsigned char*>(absorbed), x, kv_len, batch, n_q, q,
                      reinterpret_cast<unsigned char*>(workspace), reinterpret_cast<hipStream_t>(stream));
@@ -498,7 +519,7 @@ mla_status mla_attention(const mla_dims* d, const void* q, const int32_t* kv_len
   if (!aligned(q, 16) || !aligned(o_lat, 16) || (lse && !aligned(lse, 4)))
     return fail(MLA_ERR_INVALID_ARG, "q and o_lat must be 16-byte aligned");
   if ((st = check_cache(d, cache, batch))) return st;
-  const WsLayout W = ws_layout(d, batch, n_q);
+  const WsLayout W = ws_fit(d, batch, n_q, ws_bytes);
   if ((st = check_ws(W, workspace, ws_bytes))) return st;
   return attention_impl(d, W, q, kv_len, batch, n_q, cache, o_lat, lse, reinterpret_cast<unsigned char*>(workspace),
                         reinterpret_cast<hipStream_t>(stream));
@@ -513,7 +534,7 @@ mla_status mla_decode(const mla_dims* d, const void* absorbed, const void* x, co
   if (!absorbed || !x || !kv_len || !o_lat) return fail(MLA_ERR_INVALID_ARG, "absorbed, x, kv_len and o_lat must be non-NULL");
   if (!aligned(x, 16) || !aligned(o_lat, 16)) return fail(MLA_ERR_INVALID_ARG, "x and o_lat must be 16-byte aligned");
   if ((st = check_cache(d, cache, batch))) return st;
-  const WsLayout W = ws_layout(d, batch, n_q);
+  const WsLayout W = ws_fit(d, batch, n_q, ws_bytes);
   if ((st = check_ws(W, workspace, ws_bytes))) return st;
   unsigned char* ws = reinterpret_cast<unsigned char*>(workspace);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -528,7 +549,7 @@ mla_status mla_out_proj(const mla_dims* d, const void* absorbed, const float* o_
   if (st) return st;
   if (!absorbed || !o_lat || !y) return fail(MLA_ERR_INVALID_ARG, "absorbed, o_lat and y must be non-NULL");
   if (!aligned(o_lat, 16) || !aligned(y, 16)) return fail(MLA_ERR_INVALID_ARG, "o_lat and y must be 16-byte aligned");
-  const WsLayout W = ws_layout(d, n_tok, 1);
+  const WsLayout W = ws_fit(d, n_tok, 1, ws_bytes);
   if ((st = check_ws(W, workspace, ws_bytes))) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool bf = is_bf16(d);
@@ -571,7 +592,7 @@ mla_status mla_prefill_expanded(const mla_dims* d, const void* absorbed, const v
   if (!aligned(x, 16) || !aligned(y, 16)) return fail(MLA_ERR_INVALID_ARG, "x and y must be 16-byte aligned");
   if ((st = check_cache(d, cache, batch))) return st;
   if (cache->page_table) return fail(MLA_ERR_UNSUPPORTED, "expanded prefill reads a contiguous cache");
-  const PfLayout P = pf_layout(d, batch, n_q, cache->s_max);
+  const PfLayout P = pf_fit(d, batch, n_q, cache->s_max, ws_bytes);
   if (!workspace || !aligned(workspace, 256)) return fail(MLA_ERR_INVALID_ARG, "workspace must be non-NULL and 256-byte aligned");
   if (ws_bytes < P.total) return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, P.total);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);

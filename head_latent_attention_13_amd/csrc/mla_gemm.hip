@@ -790,7 +790,8 @@ static int ceil_div(int a, int b) { return (a + b - 1) / b; }
 // tried for the output projection; 1 only for one-tile A column groups).
 static const int kDecodeNT[] = {1, 2, 4, 5, 8, 9, 10};
 
-GemmPlan plan_gemm(int M, int K, int N, bool bf16, bool a_f32, int n_cu, int a_gtiles, int a_gstride) {
+GemmPlan plan_gemm(int M, int K, int N, bool bf16, bool a_f32, int n_cu, int a_gtiles, int a_gstride,
+                   size_t part_cap) {
   GemmPlan g{};
   g.M = M; g.K = K; g.N = N;
   g.a_gtiles = a_gtiles; g.a_gstride = a_gstride;
@@ -820,6 +821,7 @@ GemmPlan plan_gemm(int M, int K, int N, bool bf16, bool a_f32, int n_cu, int a_g
     for (int ks = 1; ks <= ksmax; ++ks) {
       const int kbs = ceil_div(g.kblocks, ks);
       if (ceil_div(g.kblocks, kbs) != ks) continue;
+      if (ks > 1 && (double)ks * M * g.Np * 4.0 > (double)part_cap) continue;  // partials must fit
       const long blocks = (long)gx * gy * ks;
       // per k-block a block streams `cols` weight fragments; an fp32 A
       // operand (the output projection's, large and re-read by every column
@@ -857,6 +859,7 @@ GemmPlan plan_gemm(int M, int K, int N, bool bf16, bool a_f32, int n_cu, int a_g
       // fewer blocks than about 0.8 CUs
       const long want = (long)(0.8 * n_cu);
       if (blocks0 < want) ks = (int)std::min<long>((want + blocks0 - 1) / blocks0, std::max(1, g.kblocks / 4));
+      while (ks > 1 && (double)ks * M * g.Np * 4.0 > (double)part_cap) --ks;  // partials must fit
     } else {
       // Blocks run in rounds of n_cu * occ resident blocks (occ from the
       // LDS ring); every round costs the streaming time of one block, a
@@ -870,6 +873,7 @@ GemmPlan plan_gemm(int M, int K, int N, bool bf16, bool a_f32, int n_cu, int a_g
       for (int k = 1; k <= std::max(1, g.kblocks / (2 * skb)); ++k) {
         const int kbs = ceil_div(ceil_div(g.kblocks, k), skb) * skb;
         if (ceil_div(g.kblocks, kbs) != k) continue;
+        if (k > 1 && (double)k * M * g.Np * 4.0 > (double)part_cap) continue;  // partials must fit
         const long rounds = (blocks0 * k + slots - 1) / slots;
         double cost = (double)rounds * kbs;  // k-blocks streamed by the busiest slot
         // (partials: written, read back by a second launch; weighted double)

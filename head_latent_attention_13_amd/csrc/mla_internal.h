@@ -60,9 +60,12 @@ struct GemmPlan {
 };
 
 // a_f32: the A operand is fp32 (converted to bf16 fragments in the kernel).
-// a_gtiles / a_gstride: A column groups (0: none).  Returns a plan with
-// tiled == -1 when no kernel configuration fits the groups.
-GemmPlan plan_gemm(int M, int K, int N, bool bf16, bool a_f32, int n_cu, int a_gtiles = 0, int a_gstride = 0);
+// a_gtiles / a_gstride: A column groups (0: none).  part_cap: the most bytes
+// the fp32 split-K partials may take (K splits that need more are not
+// considered; an unsplit plan needs none).  Returns a plan with tiled == -1
+// when no kernel configuration fits the groups.
+GemmPlan plan_gemm(int M, int K, int N, bool bf16, bool a_f32, int n_cu, int a_gtiles = 0, int a_gstride = 0,
+                   size_t part_cap = SIZE_MAX);
 
 // fp32 -> bf16 copy (round to nearest even); n a multiple of 8, both
 // pointers 16-byte aligned.

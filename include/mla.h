@@ -172,7 +172,10 @@ mla_status mla_absorb_weights(const mla_dims *dims, const mla_raw_weights *raw, 
 
 /* Workspace bytes needed by mla_compress_append / mla_q_proj /
  * mla_attention / mla_decode / mla_out_proj for up to `batch` sequences of
- * `n_q` new tokens on the current device (host only).  The first 256 bytes
+ * `n_q` new tokens on the current device (host only).  A call with fewer
+ * rows chooses its GEMMs' K splits so that their fp32 partials fit the
+ * workspace it is given (the splits a call would choose on its own vary
+ * with the row count).  The first 256 bytes
  * hold the device error word: zero the whole workspace once before first
  * use; later calls keep it sticky until mla_read_device_error clears it. */
 mla_status mla_workspace_size(const mla_dims *dims, int32_t batch, int32_t n_q, size_t *bytes);

@@ -185,3 +185,31 @@ def test_synthetic_bf16_rounding_matches_torch():
     a[:4] = [1.00390625, 1.01171875, -2.00390625, 0.0]  # exact ties
     ref = torch.from_numpy(a).to(torch.bfloat16).to(torch.float32).numpy()
     assert np.array_equal(round_bf16(a), ref)
+
+
+@pytest.mark.parametrize("d_model,form", [(5120, "merged"), (5120, "factored"), (7168, "merged"), (7168, "factored")])
+def test_smaller_calls_fit_the_sized_workspace(d_model, form):
+    """A workspace of mla_workspace_size(batch, 1) bytes serves every call
+    with fewer rows (the split-K partials a plan wants vary with the row
+    count, so a call plans its K splits to fit): the calls pass every host
+    check and fail only at the launch, as there is no GPU here."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("launches with placeholder device pointers: host-only check")
+    lib = _lib()
+    d = mla.make_dims(d_model, 128, 512, 1536, 128, 64, 128, "bf16", form=form)
+    ws = ctypes.c_void_p(0x100000)
+    cache = mla._lib.mla_cache(0x1000, None, 0, 0, 0, 4096)
+    p = ctypes.c_void_p(0x1000)
+    for M in (23, 64, 130, 300):
+        ws_bytes = ctypes.c_size_t(mla.mla_workspace_size(d, M, 1))
+        for m in sorted({1, 7, 16, 17, 20, 22, M // 2, M - 1}):
+            calls = {
+                "out_proj": lib.mla_out_proj(ctypes.byref(d), p, p, m, p, ws, ws_bytes, None),
+                "q_proj": lib.mla_q_proj(ctypes.byref(d), p, p, p, m, 1, p, ws, ws_bytes, None),
+                "append": lib.mla_compress_append(ctypes.byref(d), p, p, p, m, 1, ctypes.byref(cache), ws, ws_bytes,
+                                                  None),
+            }
+            for name, st in calls.items():
+                assert st == -3, (M, m, name, st, lib.mla_last_error())  # MLA_ERR_HIP: no device to launch on
+        assert lib.mla_out_proj(ctypes.byref(d), p, p, M, p, ws, ctypes.c_size_t(1024), None) == -4
