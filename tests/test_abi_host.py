@@ -213,3 +213,23 @@ def test_smaller_calls_fit_the_sized_workspace(d_model, form):
             for name, st in calls.items():
                 assert st == -3, (M, m, name, st, lib.mla_last_error())  # MLA_ERR_HIP: no device to launch on
         assert lib.mla_out_proj(ctypes.byref(d), p, p, M, p, ws, ctypes.c_size_t(1024), None) == -4
+
+
+def test_smaller_prefill_calls_fit_the_sized_workspace():
+    """The same contract for the expanded prefill: a workspace of
+    mla_prefill_workspace_size(batch, n_q, s_max) bytes serves calls with
+    fewer sequences or new tokens (host checks pass; the launch fails, as
+    there is no GPU here)."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("launches with placeholder device pointers: host-only check")
+    lib = _lib()
+    d = mla.make_dims(7168, 128, 512, 1536, 128, 64, 128, "bf16", form="factored")
+    ws = ctypes.c_void_p(0x100000)
+    cache = mla._lib.mla_cache(0x1000, None, 0, 0, 0, 5120)
+    p = ctypes.c_void_p(0x1000)
+    ws_bytes = ctypes.c_size_t(mla.mla_prefill_workspace_size(d, 2, 1024, 5120))
+    for batch, n_q in ((2, 1024), (1, 1024), (2, 300), (1, 17), (2, 1)):
+        st = lib.mla_prefill_expanded(ctypes.byref(d), p, p, p, batch, n_q, ctypes.byref(cache), p, None, ws, ws_bytes,
+                                      None)
+        assert st == -3, (batch, n_q, st, lib.mla_last_error())
