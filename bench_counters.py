@@ -18,7 +18,7 @@ profiles/mfma_<workload>.txt and, for the default workload,
 profiles/hbm_traffic.txt and profiles/mfma.txt (JSON read by bench.py: HBM
 bytes and MFMA counters per call, tagged with a hash of the kernel sources).
 
-    python bench_counters.py [--config 1] [--out gpurun_out/counters]
+    python bench_counters.py [--config 1] [--out <dir for the raw profiler output>]
 """
 from __future__ import annotations
 
@@ -29,6 +29,7 @@ import json
 import os
 import subprocess
 import sys
+import tempfile
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CALLS = ("mla_compress_append", "mla_q_proj", "mla_attention", "mla_out_proj")
@@ -154,7 +155,7 @@ def trace_durations(path, skip=5):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--config", type=int, default=1)
-    ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "counters"))
+    ap.add_argument("--out", default=os.path.join(tempfile.gettempdir(), "mla_counters"))
     ap.add_argument("--profiles-dir", default=os.path.join(ROOT, "profiles"))
     ap.add_argument("--summarize-only", action="store_true",
                     help="rebuild the summaries from the profiler output already under --out")

@@ -62,7 +62,7 @@ extern "C" {
 typedef enum mla_status {
   MLA_OK = 0,
   MLA_ERR_INVALID_ARG = -1,  /* null / misaligned pointer, bad size */
-  MLA_ERR_UNSUPPORTED = -2,  /* dims or dtype this build has no kernel for */
+  MLA_ERR_UNSUPPORTED = -2,  /* dims or dtype the library has no kernel for */
   MLA_ERR_HIP = -3,          /* a HIP runtime call or launch failed */
   MLA_ERR_WORKSPACE = -4     /* workspace or absorbed buffer too small */
 } mla_status;
