@@ -988,11 +988,11 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, const Issue& 
 #pragma unroll
   for (int kb = 0; kb < 12; ++kb) ka[kb] = *reinterpret_cast<const bf16x8*>(tb + (kb >> 2) * kFaBlk + s_base[kb & 3]);
   __builtin_amdgcn_sched_barrier(0);  // keep the twelve reads ahead of the chain
-  // Wave priority: the matrix chains run at base priority and everything
-  // else (softmax, reads, DMA) raised, so while one wave's MFMAs occupy the
-  // SIMD's matrix unit the other wave's VALU work issues first (measured:
-  // the V3 expanded step 2.08 -> 2.045 ms; raising the MFMA sections instead
-  // changed nothing).
+  // Wave priority: the softmax runs raised, everything else at base, so
+  // while one wave's MFMAs occupy the SIMD's matrix unit the other wave's
+  // softmax issues first (measured on the V3 expanded step: 2.08 -> 2.045 ms
+  // with the reads and DMA raised as well, 2.02 ms with the softmax alone;
+  // raising the MFMA sections instead changed nothing).
   f32x16 s = f32x16{};
   __builtin_amdgcn_s_setprio(0);
 #pragma unroll
@@ -1033,6 +1033,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, const Issue& 
   for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
     for (int j = 0; j < 8; ++j) pf[ks][j] = (__bf16)x[8 * ks + j];
+  __builtin_amdgcn_s_setprio(0);
   // ---- O^T += V^T . P^T ----------------------------------------------------
   typedef short v4s __attribute__((ext_vector_type(4)));
   v4s vv[4][2][2];
@@ -1045,13 +1046,11 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, const Issue& 
         vv[dt][ks][h2] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<__attribute__((address_space(3))) v4s*>(
             MLA_LDS_PTR(const_cast<unsigned char*>(tb) + (3 + (dt >> 1)) * kFaBlk + trb[dt & 1][h2] + ks * 16 * 128)));
   __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_setprio(0);
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
       O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv[dt][ks]), pf[ks], O[dt], 0, 0, 0);
-  __builtin_amdgcn_s_setprio(2);
 }
 
 __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillArgs a) {
