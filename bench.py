@@ -5,10 +5,15 @@ A step is one pass of the layer's hot path over one batch, through the C
 ABI: mla_compress_append (latent down-projection + RoPE + append),
 mla_q_proj (merged query projection), mla_attention (split-KV attention over
 the latent cache + log-sum-exp merge) and mla_out_proj (merged output
-projection).  The default workload is the DeepSeek-V2-shaped decode layer:
-batch 16, 4096 cached tokens per sequence plus the new one, contiguous bf16
-latent cache, fp32 accumulation.  Inputs are seeded and synthetic and sit in
-HBM before the timed region starts.
+projection).  The default workload is the largest single-GPU DeepSeek-V2-shaped
+decode layer: batch 64, context lengths uniform in [512, 16384], a paged bf16
+latent cache of 64-token pages, fp32 accumulation.  Inputs are seeded and
+synthetic and sit in HBM before the timed region starts.
+
+The roofline object describes the latent-cache attention (mla_attention:
+plan, split and merge kernels), the kernel the method's decode cost is
+about; its duration is the mean of per-call events over a second pass of
+the same steps (the median is reported beside it).
 
 Prints ONE JSON line (see the "roofline" and "cpu_baseline" objects).
 """
@@ -30,14 +35,17 @@ F32_PEAK_TFLOPS = 157.3      # MI355X dense fp32 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 MFMA_FILE = os.path.join(ROOT, "profiles", "mfma.txt")
 KERNEL_SOURCES = ("mla_gemm.hip", "mla_attn.hip", "mla_common.h")
+DEFAULT_CONFIG = 2
+ROOFLINE_CALL = "mla_attention"
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--config", type=int, default=1, help="workload index (1: V2 decode, B=16 x 4096)")
+    p.add_argument("--config", type=int, default=DEFAULT_CONFIG,
+                   help="workload index (2: V2 decode, B=64, paged, 512..16384 cached tokens)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--form", choices=("merged", "factored"), default="merged",
                    help="absorbed weights: merged products (default) or the factors applied at run time")
@@ -316,8 +324,10 @@ def main():
     for k in range(args.steps):
         step(k, ev[k])
     torch.cuda.synchronize()
-    per_call_ms = {c: float(np.mean([ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(args.steps)]))
-                   for i, c in enumerate(calls)}
+    call_samples = {c: [ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(args.steps)] for i, c in enumerate(calls)}
+    per_call_ms = {c: float(np.mean(v)) for c, v in call_samples.items()}
+    per_call_median_ms = {c: float(np.median(v)) for c, v in call_samples.items()}
+    step_median_ms = float(np.median([ev[k][0].elapsed_time(ev[k][-1]) for k in range(args.steps)]))
     assert all(ly.device_error() == 0 and ly.prefill_error() == 0 for ly in layers)
 
     # ---- algorithmic bytes / flops per call (one step) ------------------
@@ -367,19 +377,22 @@ def main():
         t_hbm = algo[c]["bytes"] / (HBM_PEAK_GBS * 1e9)
         t_mfma = algo[c]["flops"] / (mfma_peak * 1e12)
         bound = "hbm" if t_hbm >= t_mfma else "mfma"
-        kernels[c] = {"ms": round(per_call_ms[c], 4), "bound": bound, "GB_s": round(gbs, 1),
+        kernels[c] = {"ms": round(per_call_ms[c], 4), "ms_median": round(per_call_median_ms[c], 4), "bound": bound,
+                      "GB_s": round(gbs, 1),
                       "TFLOP_s": round(tfl, 2), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                       "mfma_frac": round(tfl / mfma_peak, 4),
                       "roofline_frac": round((t_hbm if bound == "hbm" else t_mfma) / t, 4)}
-    dom = max(calls, key=lambda c: per_call_ms[c])
+    dom = "mla_prefill_expanded" if expanded else ROOFLINE_CALL
     d = kernels[dom]
     traffic = measured_traffic(dom, cfg.name)
     if d["bound"] == "hbm":
         roofline = {"bound": "hbm", "achieved": d["GB_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(d["GB_s"] / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom}
+                    "frac": round(d["GB_s"] / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom,
+                    "algorithmic_bytes": algo[dom]["bytes"], "ms": d["ms"]}
     else:
         roofline = {"bound": "mfma", "achieved": d["TFLOP_s"], "peak": mfma_peak, "unit": "TFLOP/s",
-                    "frac": round(d["TFLOP_s"] / mfma_peak, 4), "traffic": traffic, "kernel": dom}
+                    "frac": round(d["TFLOP_s"] / mfma_peak, 4), "traffic": traffic, "kernel": dom,
+                    "algorithmic_flops": algo[dom]["flops"], "ms": d["ms"]}
     att = kernels["mla_prefill_expanded" if expanded else "mla_attention"]
 
     out = {
@@ -390,6 +403,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "ms_per_step_median_marked": round(step_median_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

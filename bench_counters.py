@@ -14,11 +14,11 @@ Runs, each as its own rocprofv3 process with the program directly after
      call and the fraction of SIMD cycles the matrix units were busy.
 
 Writes profiles/kernel_stats_<workload>.txt, profiles/hbm_traffic_<workload>.txt,
-profiles/mfma_<workload>.txt and, for the default workload,
+profiles/mfma_<workload>.txt and, for bench.py's default workload,
 profiles/hbm_traffic.txt and profiles/mfma.txt (JSON read by bench.py: HBM
 bytes and MFMA counters per call, tagged with a hash of the kernel sources).
 
-    python bench_counters.py [--config 1] [--out <dir for the raw profiler output>]
+    python bench_counters.py [--config N] [--out <dir for the raw profiler output>]
 """
 from __future__ import annotations
 
@@ -154,12 +154,16 @@ def trace_durations(path, skip=5):
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--config", type=int, default=None, help="workload index (default: bench.py's)")
     ap.add_argument("--out", default=os.path.join(tempfile.gettempdir(), "mla_counters"))
     ap.add_argument("--profiles-dir", default=os.path.join(ROOT, "profiles"))
     ap.add_argument("--summarize-only", action="store_true",
                     help="rebuild the summaries from the profiler output already under --out")
     args = ap.parse_args()
+    sys.path.insert(0, ROOT)
+    import bench
+    if args.config is None:
+        args.config = bench.DEFAULT_CONFIG
     # the profiler runs from /tmp: every path handed to it is absolute
     args.out = os.path.abspath(args.out)
     args.profiles_dir = os.path.abspath(args.profiles_dir)
@@ -282,8 +286,7 @@ def main():
             f.write(f"# {c}: {m['flops'] / 1e9:.3f} GFLOP counted, {m['flops'] / (m['us'] * 1e-6) / 1e12:.1f} TFLOP/s "
                     f"({100 * m['flops'] / (m['us'] * 1e-6) / 2.5e15:.2f}% of peak), MFMA busy "
                     f"{100 * m['busy'] / max(m['active'], 1):.2f}% of SIMD cycles\n")
-    if args.config == 1:
-        import bench
+    if args.config == bench.DEFAULT_CONFIG:
         mout = {"workload": workload, "source_hash": bench.kernel_source_hash(), "flops_per_mop": flops_per_mop,
                 "calls": {c: {"gflop": round(m["flops"] / 1e9, 4),
                               "busy_pct": round(100 * m["busy"] / max(m["active"], 1), 2)} for c, m in mcalls.items()}}

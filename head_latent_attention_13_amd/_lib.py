@@ -60,6 +60,10 @@ _SIGS = {
                                             ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "mla_workspace_size": (ctypes.c_int32, [ctypes.POINTER(mla_dims), ctypes.c_int32, ctypes.c_int32,
                                             ctypes.POINTER(ctypes.c_size_t)]),
+    "mla_workspace_check": (ctypes.c_int32, [ctypes.POINTER(mla_dims), ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.c_size_t]),
+    "mla_prefill_workspace_check": (ctypes.c_int32, [ctypes.POINTER(mla_dims), ctypes.c_int32, ctypes.c_int32,
+                                                     ctypes.c_int32, ctypes.c_size_t]),
     "mla_read_device_error": (ctypes.c_int32, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32), ctypes.c_void_p]),
     "mla_compress_append": (ctypes.c_int32, [ctypes.POINTER(mla_dims), ctypes.c_void_p, ctypes.c_void_p,
                                              ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
@@ -164,6 +168,18 @@ def mla_workspace_size(dims: mla_dims, batch: int, n_q: int) -> int:
     n = ctypes.c_size_t()
     _check("mla_workspace_size", load().mla_workspace_size(ctypes.byref(dims), batch, n_q, ctypes.byref(n)))
     return n.value
+
+
+def mla_workspace_check(dims: mla_dims, batch: int, n_q: int, ws_bytes: int) -> int:
+    """Status (0 = fits) of the decode-path calls for batch x n_q rows on a
+    workspace of ws_bytes (host only)."""
+    return load().mla_workspace_check(ctypes.byref(dims), batch, n_q, ws_bytes)
+
+
+def mla_prefill_workspace_check(dims: mla_dims, batch: int, n_q: int, s_max: int, ws_bytes: int) -> int:
+    """Status (0 = fits) of mla_prefill_expanded for these sizes on a
+    workspace of ws_bytes (host only)."""
+    return load().mla_prefill_workspace_check(ctypes.byref(dims), batch, n_q, s_max, ws_bytes)
 
 
 def mla_read_device_error(workspace: torch.Tensor, stream=None) -> int:

@@ -457,6 +457,15 @@ mla_status mla_workspace_size(const mla_dims* d, int32_t batch, int32_t n_q, siz
   return MLA_OK;
 }
 
+mla_status mla_workspace_check(const mla_dims* d, int32_t batch, int32_t n_q, size_t ws_bytes) {
+  mla_status st = check_common(d, nullptr, batch, n_q);
+  if (st) return st;
+  const WsLayout W = ws_fit(d, batch, n_q, ws_bytes);
+  if (!W.plans_ok) return fail(MLA_ERR_UNSUPPORTED, "no GEMM configuration fits the per-head factored products");
+  if (ws_bytes < W.total) return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, W.total);
+  return MLA_OK;
+}
+
 mla_status mla_read_device_error(void* workspace, int32_t* flags, void* stream) {
   if (!workspace || !flags) return fail(MLA_ERR_INVALID_ARG, "workspace and flags must be non-NULL");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -578,6 +587,14 @@ mla_status mla_prefill_workspace_size(const mla_dims* d, int32_t batch, int32_t 
   if (st) return st;
   if (!bytes) return fail(MLA_ERR_INVALID_ARG, "bytes is NULL");
   *bytes = pf_layout(d, batch, n_q, s_max).total;
+  return MLA_OK;
+}
+
+mla_status mla_prefill_workspace_check(const mla_dims* d, int32_t batch, int32_t n_q, int32_t s_max, size_t ws_bytes) {
+  mla_status st = check_prefill(d, batch, n_q, s_max);
+  if (st) return st;
+  const PfLayout P = pf_fit(d, batch, n_q, s_max, ws_bytes);
+  if (ws_bytes < P.total) return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, P.total);
   return MLA_OK;
 }
 

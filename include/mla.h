@@ -180,6 +180,15 @@ mla_status mla_absorb_weights(const mla_dims *dims, const mla_raw_weights *raw, 
  * use; later calls keep it sticky until mla_read_device_error clears it. */
 mla_status mla_workspace_size(const mla_dims *dims, int32_t batch, int32_t n_q, size_t *bytes);
 
+/* Whether a workspace of ws_bytes serves mla_compress_append, mla_q_proj,
+ * mla_attention, mla_decode and mla_out_proj for batch x n_q rows (host
+ * only; nothing is enqueued).  Returns MLA_OK, or the status those calls
+ * return before enqueueing anything for that size (MLA_ERR_WORKSPACE when
+ * the bytes do not fit, MLA_ERR_UNSUPPORTED when no GEMM configuration fits
+ * the dims, MLA_ERR_INVALID_ARG for bad dims or sizes).  The workspace
+ * pointer itself is not needed. */
+mla_status mla_workspace_check(const mla_dims *dims, int32_t batch, int32_t n_q, size_t ws_bytes);
+
 /* Reads (and clears) the device error word of a workspace; synchronises
  * `stream`.  *flags (host) receives a bit mask: 1 = position outside the
  * cache, 2 = page id outside [0, n_pages), 4 = kv_len outside
@@ -243,6 +252,12 @@ mla_status mla_out_proj(const mla_dims *dims, const void *absorbed, const float 
  * in mla_workspace_size: zero the workspace once before first use. */
 mla_status mla_prefill_workspace_size(const mla_dims *dims, int32_t batch, int32_t n_q, int32_t s_max,
                                       size_t *bytes);
+
+/* Whether a workspace of ws_bytes serves mla_prefill_expanded for batch
+ * sequences of n_q new tokens over a contiguous cache of s_max rows per
+ * sequence (host only, as mla_workspace_check). */
+mla_status mla_prefill_workspace_check(const mla_dims *dims, int32_t batch, int32_t n_q, int32_t s_max,
+                                       size_t ws_bytes);
 
 /* Chunked prefill in the expanded form (for long query chunks, where the
  * attention is bound by matrix throughput): every cached latent c_i is

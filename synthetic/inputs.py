@@ -125,11 +125,38 @@ def make_page_table(kv_len: np.ndarray, page_size: int, rng: np.random.Generator
     return table, n_pages
 
 
-def make_rows(cfg: MLAConfig, lengths: np.ndarray, rng: np.random.Generator) -> List[np.ndarray]:
-    """Synthetic cache rows per sequence, as fp32 arrays [S_b, R]."""
+def quiet_then_loud(n_rows: int, quiet_rows: int = 32, quiet: float = 0.05, lo: float = 5.0,
+                    hi: float = 6.0) -> np.ndarray:
+    """Per-row amplitude multipliers: the first ``quiet_rows`` rows scaled by
+    ``quiet``, the rest by a linear ramp from ``lo`` to ``hi``.
+
+    A cache of such rows makes every head's largest score jump by many times
+    the unscaled score spread between the first 32-row block of a sequence
+    and the next, and keeps growing along the sequence; it is an input
+    pattern only (the amplitudes multiply i.i.d. normal draws).
+    """
+    a = np.empty(n_rows, dtype=np.float32)
+    q = min(quiet_rows, n_rows)
+    a[:q] = quiet
+    if n_rows > q:
+        a[q:] = np.linspace(lo, hi, n_rows - q, dtype=np.float32)
+    return a
+
+
+def make_rows(cfg: MLAConfig, lengths: np.ndarray, rng: np.random.Generator,
+              amplitude=None) -> List[np.ndarray]:
+    """Synthetic cache rows per sequence, as fp32 arrays [S_b, R].
+
+    ``amplitude``: optional callable n -> [n] per-row multipliers (applied
+    to the fp32 draws before the bf16 rounding)."""
     std = np.float32(row_std(cfg))
-    return [_finish(rng.standard_normal((int(s), cfg.row), dtype=np.float32) * std, cfg)
-            for s in lengths]
+    out = []
+    for s in lengths:
+        r = rng.standard_normal((int(s), cfg.row), dtype=np.float32) * std
+        if amplitude is not None:
+            r *= np.asarray(amplitude(int(s)), np.float32)[:, None]
+        out.append(_finish(r, cfg))
+    return out
 
 
 def make_x(cfg: MLAConfig, shape, rng: np.random.Generator) -> np.ndarray:
@@ -161,7 +188,9 @@ class Case:
 
 
 def make_case(cfg: MLAConfig, seed: int, history: str = "rows",
-              spare_pages: int = 0) -> Case:
+              spare_pages: int = 0, amplitude=None) -> Case:
+    """``amplitude``: optional per-row multipliers of the history rows
+    (history="rows" only; see quiet_then_loud)."""
     rng = np.random.default_rng(seed)
     w = make_weights(cfg, rng)
     cached = make_lengths(cfg, rng)
@@ -170,7 +199,7 @@ def make_case(cfg: MLAConfig, seed: int, history: str = "rows",
         table, n_pages = make_page_table(cached + cfg.n_q, cfg.page_size, rng, spare_pages)
     rows = x_hist = None
     if history == "rows":
-        rows = make_rows(cfg, cached, rng)
+        rows = make_rows(cfg, cached, rng, amplitude)
     elif history == "x":
         x_hist = [make_x(cfg, (int(s), cfg.d_model), rng) for s in cached]
     else:

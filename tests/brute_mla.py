@@ -37,8 +37,9 @@ def decode(W, tokens, n_new, base, scale):
     """W: dict of nested lists; tokens: list of d_model lists at positions 0..T-1.
 
     The last ``n_new`` tokens are queries (causal).  Returns dict with y
-    [n_new][d_model], o_h [n_new][H][d_v], o_lat [n_new][H][d_L] and
-    p [n_new][H][T].
+    [n_new][d_model], o_h [n_new][H][d_v], o_lat [n_new][H][d_L],
+    p [n_new][H][T] and lse [n_new][H] (natural log of the softmax
+    denominator of the scaled scores).
     """
     T = len(tokens)
     d_model = len(tokens[0])
@@ -53,12 +54,12 @@ def decode(W, tokens, n_new, base, scale):
     kr = [[_vecmat(tokens[i], lambda k, r: W["W_KR"][k][r], r) for r in range(d_rope)] for i in range(T)]
     k_pe = [_rot(kr[i], i, base) for i in range(T)]
 
-    res = {"y": [], "o_h": [], "o_lat": [], "p": []}
+    res = {"y": [], "o_h": [], "o_lat": [], "p": [], "lse": []}
     for t in range(T - n_new, T):
         x = tokens[t]
         cq = [_vecmat(x, lambda k, l: W["W_DQ"][k][l], l) for l in range(d_LQ)]
         y = [[] for _ in range(d_model)]
-        o_all, ol_all, p_all = [], [], []
+        o_all, ol_all, p_all, lse_all = [], [], [], []
         for h in range(H):
             qn = [math.fsum(cq[l] * W["W_UQ"][l][h][d] for l in range(d_LQ)) for d in range(d_nope)]
             qr = [math.fsum(cq[l] * W["W_QR"][l][h][r] for l in range(d_LQ)) for r in range(d_rope)]
@@ -81,8 +82,10 @@ def decode(W, tokens, n_new, base, scale):
             o_all.append(o)
             ol_all.append(ol)
             p_all.append(p)
+            lse_all.append(mx + math.log(den))
         res["y"].append([math.fsum(terms) for terms in y])
         res["o_h"].append(o_all)
         res["o_lat"].append(ol_all)
         res["p"].append(p_all)
+        res["lse"].append(lse_all)
     return res

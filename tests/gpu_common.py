@@ -2,11 +2,14 @@
 run one layer step through the C ABI, compare against the oracle."""
 from __future__ import annotations
 
+import functools
+
 import numpy as np
 import torch
 
 import head_latent_attention_13_amd as mla
-from synthetic import Case
+from oracle import expanded as OE
+from synthetic import Case, config, make_case, quiet_then_loud
 
 DEV = "cuda"
 
@@ -61,21 +64,45 @@ def i32(a):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(DEV)
 
 
+# Canary guard bands: outputs are carved out of a larger buffer whose
+# GUARD elements on either side hold a sentinel; a write outside the output
+# changes them.
+GUARD = 4096
+SENTINEL = -12345.5
+
+
+class Guarded:
+    """An fp32 output tensor of `shape` with sentinel-filled guard bands."""
+
+    def __init__(self, *shape):
+        n = int(np.prod(shape))
+        self.buf = torch.full((n + 2 * GUARD,), SENTINEL, dtype=torch.float32, device=DEV)
+        self.t = self.buf[GUARD:GUARD + n].view(*shape)
+
+    def check(self, what="output"):
+        b = self.buf.cpu().numpy()
+        assert (b[:GUARD] == SENTINEL).all() and (b[-GUARD:] == SENTINEL).all(), f"{what}: guard band overwritten"
+
+
 def run_step(layer, cfg, case: Case, cache, do_append=True):
-    """append (optional) + decode + out_proj for the case's new tokens."""
+    """append (optional) + decode + out_proj for the case's new tokens.
+    o_lat, lse and y sit between guard bands, checked after the step."""
     B, n_q = cfg.batch, cfg.n_q
     x = dev(case.x_new.reshape(B * n_q, cfg.d_model), cfg)
     pos = i32(case.cached)
     kv = i32(case.cached + n_q)
-    o_lat = torch.empty(B * n_q, cfg.n_heads, cfg.d_latent, dtype=torch.float32, device=DEV)
-    lse = torch.empty(B * n_q, cfg.n_heads, dtype=torch.float32, device=DEV)
-    y = torch.empty(B * n_q, cfg.d_model, dtype=torch.float32, device=DEV)
+    o_lat = Guarded(B * n_q, cfg.n_heads, cfg.d_latent)
+    lse = Guarded(B * n_q, cfg.n_heads)
+    y = Guarded(B * n_q, cfg.d_model)
     if do_append:
         layer.append(x, pos, B, n_q, cache)
-    layer.decode(x, kv, B, n_q, cache, o_lat, lse)
-    layer.out_proj(o_lat, B * n_q, y)
+    layer.decode(x, kv, B, n_q, cache, o_lat.t, lse.t)
+    layer.out_proj(o_lat.t, B * n_q, y.t)
     torch.cuda.synchronize()
-    return o_lat, lse, y
+    o_lat.check("o_lat")
+    lse.check("lse")
+    y.check("y")
+    return o_lat.t, lse.t, y.t
 
 
 def rel_l2(a, b):
@@ -109,3 +136,38 @@ def unpack(buf: np.ndarray, K: int, N: int, bf16: bool) -> np.ndarray:
     a = buf.reshape(Kp // KB, Np // 16, KB // KPL, 16, KPL)      # [kb, nt, g, n16, j]
     a = a.transpose(0, 2, 4, 1, 3).reshape(Kp, Np)                # [kb, g, j, nt, n16]
     return a[:K, :N]
+
+
+def oracle_for(case: Case, b, js=None, **kw):
+    """Expanded oracle for sequence b of a case whose history is given as
+    rows: its new tokens' rows are appended, then queries js (default: all
+    new tokens) attend."""
+    cfg = case.cfg
+    S = int(case.cached[b])
+    W = case.weights
+    n_q = cfg.n_q
+    js = np.arange(n_q) if js is None else np.asarray(js)
+    c_new, k_new = OE.latent_rows(W, case.x_new[b], S + np.arange(n_q), cfg.rope_base)
+    c = np.concatenate([case.rows[b][:, :cfg.d_latent], c_new])
+    k = np.concatenate([case.rows[b][:, cfg.d_latent:], k_new])
+    _, qn, qp = OE.query(W, case.x_new[b][js], S + js, cfg.rope_base)
+    return OE.attention(W, qn, qp, c, k, S + js, cfg.softmax_scale, **kw)
+
+
+# Queries of the V3 1024-token chunk checked against the oracle: one whole
+# block of 128, the edges of later query blocks and key tiles, the last.
+CHUNK_QUERIES = np.unique(np.concatenate([np.arange(128), [129, 159, 160, 161, 255, 256, 511, 512, 767, 1022, 1023]]))
+
+
+@functools.lru_cache(maxsize=2)
+def chunk_case(seed, loud):
+    """The V3 chunked-prefill workload (seeded; ``loud``: history rows
+    following synthetic.quiet_then_loud)."""
+    return make_case(config(4), seed, amplitude=quiet_then_loud if loud else None)
+
+
+@functools.lru_cache(maxsize=4)
+def chunk_oracle(seed, loud, b):
+    """Oracle outputs (o_lat, lse, y) of CHUNK_QUERIES of sequence b of
+    chunk_case(seed, loud); shared by the absorbed and expanded tests."""
+    return oracle_for(chunk_case(seed, loud), b, CHUNK_QUERIES)

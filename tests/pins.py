@@ -30,13 +30,19 @@ def _tokens(case, b):
     return np.concatenate([case.x_hist[b], case.x_new[b]]).astype(np.float64)
 
 
-def _run_decode(E, case, b, W=None):
+def _run_decode(E, case, b, W=None, **kw):
     cfg = case.cfg
     W = case.weights if W is None else W
     S = int(case.cached[b])
     c_h, k_h = E.latent_rows(W, case.x_hist[b], np.arange(S), cfg.rope_base)
     return E.decode_step(W, cfg.rope_base, cfg.softmax_scale, case.x_new[b], S, c_h, k_h,
-                         want_p=True)
+                         want_p=True, **kw)
+
+
+# Head blocks the expanded oracle is run with by the pins: its default (one
+# block at these head counts), one head per block, and a block size that
+# leaves a ragged last block (4 of the 6 MID heads, 3 of the 4 TINY heads).
+HEAD_BLOCKS = (None, 1, 3, 4)
 
 
 # ------------------------------------------------------------------ P1 ----
@@ -67,9 +73,15 @@ def pin_mha(E, seed=11):
             V = torch.einsum("tm,mhd->htd", X, W_V)
             O = torch.nn.functional.scaled_dot_product_attention(
                 Q[None], K[None], V[None], is_causal=True, scale=cfg.softmax_scale)[0]
+            o_mha = O[:, -cfg.n_q:].transpose(0, 1).numpy()
             y_mha = torch.einsum("htd,hdm->tm", O, Wd["W_O"])[-cfg.n_q:].numpy()
-            out = _run_decode(E, case, b, W)
-            worst = max(worst, _rel(out["y"], y_mha))
+            for hb in HEAD_BLOCKS:
+                out = _run_decode(E, case, b, W, head_block=hb)
+                worst = max(worst, _rel(out["y"], y_mha), _rel(out["o_h"], o_mha))
+            # a subset of heads, in a scrambled order, in blocks of two
+            hs = [H - 1, 0, H // 2]
+            sub = _run_decode(E, case, b, W, heads=hs, head_block=2)
+            worst = max(worst, _rel(sub["o_h"], o_mha[:, hs]))
     return worst
 
 
@@ -128,9 +140,25 @@ def pin_brute(E, seed=14):
     Wl = {k: np.asarray(v, np.float64).tolist() for k, v in case.weights.items()}
     toks = _tokens(case, 0)
     bf = brute_mla.decode(Wl, toks.tolist(), cfg.n_q, cfg.rope_base, cfg.softmax_scale)
-    out = _run_decode(E, case, 0)
-    return max(_rel(out["y"], bf["y"]), _rel(out["o_h"], bf["o_h"]),
-               _rel(out["o_lat"], bf["o_lat"]), _rel(out["p"], bf["p"]))
+    worst = 0.0
+    for hb in HEAD_BLOCKS:
+        out = _run_decode(E, case, 0, head_block=hb)
+        worst = max(worst, _rel(out["y"], bf["y"]), _rel(out["o_h"], bf["o_h"]), _rel(out["o_lat"], bf["o_lat"]),
+                    _rel(out["p"], bf["p"]), _rel(out["lse"], bf["lse"]))
+    # a subset of heads, in a scrambled order, in blocks of one and of two:
+    # each head's outputs equal the brute force's for that head, and the
+    # partial output projection is the subset's share of y
+    H = cfg.n_heads
+    hs = [H - 1, 1]
+    o_ref = np.asarray(bf["o_h"])[:, hs]
+    W_O = np.asarray(case.weights["W_O"], np.float64)
+    y_part = sum(o_ref[:, i] @ W_O[h] for i, h in enumerate(hs))
+    for hb in (1, 2):
+        sub = _run_decode(E, case, 0, heads=hs, head_block=hb)
+        worst = max(worst, _rel(sub["o_h"], o_ref), _rel(sub["o_lat"], np.asarray(bf["o_lat"])[:, hs]),
+                    _rel(sub["p"], np.asarray(bf["p"])[:, hs]), _rel(sub["lse"], np.asarray(bf["lse"])[:, hs]),
+                    _rel(sub["y_partial"], y_part))
+    return worst
 
 
 # ------------------------------------------------------------------ P5 ----

@@ -18,8 +18,8 @@ from oracle import absorbed as OA
 from oracle import expanded as OE
 from synthetic import Case, config, make_case, make_rows, make_x
 
-from .gpu_common import (DEV, assert_close, contiguous_cache, dev, dims_of, i32, paged_cache, run_step, tdtype,
-                         unpack, upload_weights)
+from .gpu_common import (CHUNK_QUERIES, DEV, assert_close, chunk_case, chunk_oracle, contiguous_cache, dev, dims_of,
+                         i32, paged_cache, run_step, tdtype, unpack, upload_weights)
 
 pytestmark = pytest.mark.gpu
 
@@ -213,7 +213,7 @@ def test_v2_long_context_split_kv():
 
 # ---------------------------------------------------- V3 chunked prefill ----
 def test_v3_chunked_prefill_causal():
-    case = case_of(4)
+    case = chunk_case(4, False)
     cfg = case.cfg
     n_q = cfg.n_q
     note("v3 prefill: absorb + cache")
@@ -221,22 +221,15 @@ def test_v3_chunked_prefill_causal():
     cache, _ = contiguous_cache(cfg, case.rows, int(case.cached.max()) + n_q)
     note("v3 prefill: chunk step")
     o_lat, lse, y = run_step(layer, cfg, case, cache)
-    o_lat = o_lat.view(cfg.batch, n_q, cfg.n_heads, cfg.d_latent)
-    lse = lse.view(cfg.batch, n_q, cfg.n_heads)
-    y = y.view(cfg.batch, n_q, cfg.d_model)
-    b = 1
-    S = int(case.cached[b])
-    js = np.array([0, 1, 511, 1023])
-    W = case.weights
-    xs = case.x_new[b]
-    c_new, k_new = OE.latent_rows(W, xs, S + np.arange(n_q), cfg.rope_base)
-    c = np.concatenate([case.rows[b][:, :cfg.d_latent], c_new])
-    k = np.concatenate([case.rows[b][:, cfg.d_latent:], k_new])
-    _, qn, qp = OE.query(W, xs[js], S + js, cfg.rope_base)
-    ref = OE.attention(W, qn, qp, c, k, S + js, cfg.softmax_scale)
-    assert_close(o_lat.cpu().numpy()[b][js], ref["o_lat"], cfg, "o_lat (sampled queries)")
-    assert_close(lse.cpu().numpy()[b][js], ref["lse"], cfg, "lse (sampled queries)")
-    assert_close(y.cpu().numpy()[b][js], ref["y"], cfg, "y (sampled queries)")
+    o_lat = o_lat.view(cfg.batch, n_q, cfg.n_heads, cfg.d_latent).cpu().numpy()
+    lse = lse.view(cfg.batch, n_q, cfg.n_heads).cpu().numpy()
+    y = y.view(cfg.batch, n_q, cfg.d_model).cpu().numpy()
+    js = CHUNK_QUERIES
+    for b in range(cfg.batch):
+        ref = chunk_oracle(4, False, b)
+        assert_close(o_lat[b][js], ref["o_lat"], cfg, f"o_lat[b={b}] ({len(js)} queries)")
+        assert_close(lse[b][js], ref["lse"], cfg, f"lse[b={b}]")
+        assert_close(y[b][js], ref["y"], cfg, f"y[b={b}]")
 
 
 # ------------------------------------------------------------ edge cases ----

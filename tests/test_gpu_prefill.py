@@ -17,7 +17,8 @@ import head_latent_attention_13_amd as mla
 from oracle import expanded as OE
 from synthetic import Case, config, make_case, make_rows, make_x
 
-from .gpu_common import DEV, assert_close, contiguous_cache, dev, dims_of, i32, run_step, upload_weights
+from .gpu_common import (CHUNK_QUERIES, DEV, assert_close, chunk_case, chunk_oracle, contiguous_cache, dev, dims_of,
+                         i32, run_step, upload_weights)
 
 pytestmark = pytest.mark.gpu
 
@@ -46,7 +47,7 @@ def prefill(layer, cfg, case, cache):
 
 
 def test_prefill_v3_chunk_sampled_and_vs_absorbed():
-    case = make_case(config(4), 4)
+    case = chunk_case(4, False)
     cfg = case.cfg
     n_q = cfg.n_q
     note("prefill v3: pack + cache")
@@ -56,17 +57,11 @@ def test_prefill_v3_chunk_sampled_and_vs_absorbed():
     y, lse = prefill(layer, cfg, case, cache)
     y = y.view(cfg.batch, n_q, cfg.d_model).cpu().numpy()
     lse = lse.view(cfg.batch, n_q, cfg.n_heads).cpu().numpy()
-    for b, js in ((0, np.array([0, 1, 127, 128, 1023])), (1, np.array([5, 511, 900]))):
-        S = int(case.cached[b])
-        W = case.weights
-        xs = case.x_new[b]
-        c_new, k_new = OE.latent_rows(W, xs, S + np.arange(n_q), cfg.rope_base)
-        c = np.concatenate([case.rows[b][:, :cfg.d_latent], c_new])
-        k = np.concatenate([case.rows[b][:, cfg.d_latent:], k_new])
-        _, qn, qp = OE.query(W, xs[js], S + js, cfg.rope_base)
-        ref = OE.attention(W, qn, qp, c, k, S + js, cfg.softmax_scale)
-        assert_close(y[b][js], ref["y"], cfg, f"y[b={b}] (sampled queries)")
-        assert_close(lse[b][js], ref["lse"], cfg, f"lse[b={b}] (sampled queries)")
+    js = CHUNK_QUERIES
+    for b in range(cfg.batch):
+        ref = chunk_oracle(4, False, b)
+        assert_close(y[b][js], ref["y"], cfg, f"y[b={b}] ({len(js)} queries)")
+        assert_close(lse[b][js], ref["lse"], cfg, f"lse[b={b}]")
     # the absorbed form of the same layer on every token
     note("prefill v3: absorbed form")
     _, lse_a, y_a = run_step(layer, cfg, case, cache, do_append=False)

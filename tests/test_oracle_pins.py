@@ -128,6 +128,13 @@ MUTATIONS = [
     ("rope", "a * sin + b * cos", "-a * sin + b * cos"),                             # sign
     ("rope", "a, b = v[..., 0::2], v[..., 1::2]", "a, b = v[..., 1::2], v[..., 0::2]"),  # pair order
     ("rope", "-2.0 * j / d_rope", "-1.0 * j / d_rope"),                              # frequencies
+    # head blocks: a block's results stored at the wrong offset, every block
+    # computed for the first block's heads, the subset's head list ignored
+    ("expanded", "o_lat[:, s:s + len(blk)] =", "o_lat[:, 0:len(blk)] ="),
+    ("expanded", "o_h[:, s:s + len(blk)] =", "o_h[:, 0:len(blk)] ="),
+    ("expanded", "lse[:, s:s + len(blk)] =", "lse[:, 0:len(blk)] ="),
+    ("expanded", "blk = hs[s:s + head_block]", "blk = hs[0:head_block]"),
+    ("expanded", "hs = list(range(H)) if heads is None else list(heads)", "hs = list(range(H))"),
     ("absorbed", "W_UQ[:, h, :] @ W_UK[:, h, :].T", "W_UQ[:, h, :] @ W_UK[:, -h - 1, :].T"),
     ("absorbed", "W_UV[:, h, :] @ W_O[h]", "W_UV[:, h, :] @ W_O[(h + 1) % len(W_O)]"),
 ]
