@@ -114,14 +114,20 @@ def max_abs(a, b):
     return float(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64)).max())
 
 
-def assert_close(gpu, ref, cfg, what):
+def assert_close(gpu, ref, cfg, what, stress=False):
+    """rel-L2 and max-abs bars of the configuration's dtype.  ``stress``:
+    inputs scaled beyond the workloads' distribution (the rebase rows), for
+    which the bf16 max-abs bar is taken relative to the reference's largest
+    magnitude, as the fp32 bar always is (the bf16 rounding of the query
+    alone moves the outputs by about 1% of their scale there)."""
     gpu = np.asarray(gpu, np.float64)
     ref = np.asarray(ref, np.float64)
     assert gpu.shape == ref.shape, (what, gpu.shape, ref.shape)
     assert np.isfinite(gpu).all(), f"{what}: non-finite GPU values"
     r, m = rel_l2(gpu, ref), max_abs(gpu, ref)
     if cfg.dtype == "bf16":
-        ok = r <= BF16_REL_L2 and m <= BF16_MAX_ABS
+        scale = max(1.0, float(np.abs(ref).max())) if stress else 1.0
+        ok = r <= BF16_REL_L2 and m <= BF16_MAX_ABS * scale
     else:
         ok = r <= F32_REL_L2 and m <= F32_MAX_ABS * max(1.0, float(np.abs(ref).max()))
     print(f"[parity] {cfg.name} {what}: rel_l2={r:.3e} max_abs={m:.3e}", flush=True)

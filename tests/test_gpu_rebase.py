@@ -13,8 +13,11 @@ precondition on the CPU from the oracle's own scores (the softmax
 definition of page "How DeepSeek Rewrote the Transformer", section 03,
 "Normalize"), then compares the GPU outputs with the oracle.
 
-Bars: rel-L2 <= 1e-2 and max-abs <= 3e-2 (bf16 cache, fp32 accumulation);
-1e-5 for the fp32 configuration.
+Bars: rel-L2 <= 1e-2 (bf16 cache, fp32 accumulation) and max-abs <= 3e-2
+relative to the reference's largest magnitude (these rows reach 6x the
+workloads' scale and the outputs with them; the bf16 rounding of the query
+alone, which the interface fixes, moves them by about 1% of that scale:
+tests/test_tolerance_model.py); 1e-5 for the fp32 configuration.
 """
 import functools
 
@@ -23,9 +26,11 @@ import pytest
 import torch
 
 import head_latent_attention_13_amd as mla
-from synthetic import Case, config, make_case, make_rows, make_x, quiet_then_loud
+from oracle import absorbed as OA
+from synthetic import (Case, config, make_case, make_lengths, make_weights, make_page_table, make_rows, make_x, quiet_then_loud,
+                       round_bf16)
 
-from .gpu_common import (CHUNK_QUERIES, Guarded, assert_close, chunk_case, chunk_oracle, contiguous_cache, dev,
+from .gpu_common import (CHUNK_QUERIES, DEV, Guarded, assert_close, chunk_case, chunk_oracle, contiguous_cache, dev,
                          dims_of, i32, oracle_for, paged_cache, run_step, upload_weights)
 
 pytestmark = pytest.mark.gpu
@@ -91,9 +96,9 @@ def test_rebase_v2_contiguous():
     for b in (0, 9, 15):
         ref = oracle_for(case, b, want_p=True)
         assert_rebases(ref, f"v2 contiguous b={b}")
-        assert_close(o_lat.cpu().numpy()[b], ref["o_lat"][0], cfg, f"o_lat[b={b}]")
-        assert_close(lse.cpu().numpy()[b], ref["lse"][0], cfg, f"lse[b={b}]")
-        assert_close(y.cpu().numpy()[b], ref["y"][0], cfg, f"y[b={b}]")
+        assert_close(o_lat.cpu().numpy()[b], ref["o_lat"][0], cfg, f"o_lat[b={b}]", stress=True)
+        assert_close(lse.cpu().numpy()[b], ref["lse"][0], cfg, f"lse[b={b}]", stress=True)
+        assert_close(y.cpu().numpy()[b], ref["y"][0], cfg, f"y[b={b}]", stress=True)
     assert layer.device_error() == 0
 
 
@@ -116,31 +121,79 @@ def test_rebase_v2_paged():
     for b in (int(order[0]), int(order[len(order) // 2]), int(order[-1])):
         ref = oracle_for(case, b, want_p=True)
         assert_rebases(ref, f"v2 paged b={b}")
-        assert_close(o_lat.cpu().numpy()[b], ref["o_lat"][0], cfg, f"o_lat[b={b}, len={kv[b]}]")
-        assert_close(lse.cpu().numpy()[b], ref["lse"][0], cfg, f"lse[b={b}]")
-        assert_close(y.cpu().numpy()[b], ref["y"][0], cfg, f"y[b={b}]")
+        assert_close(o_lat.cpu().numpy()[b], ref["o_lat"][0], cfg, f"o_lat[b={b}, len={kv[b]}]", stress=True)
+        assert_close(lse.cpu().numpy()[b], ref["lse"][0], cfg, f"lse[b={b}]", stress=True)
+        assert_close(y.cpu().numpy()[b], ref["y"][0], cfg, f"y[b={b}]", stress=True)
     assert layer.device_error() == 0
 
 
-def test_rebase_v3_chunk_absorbed():
-    case = chunk_case(104, True)
-    cfg = case.cfg
-    n_q = cfg.n_q
-    layer = mla.MLALayer(dims_of(cfg), upload_weights(case), max_batch=cfg.batch, max_nq=n_q)
-    cache, _ = contiguous_cache(cfg, case.rows, int(case.cached.max()) + n_q)
-    note("rebase v3 chunk (absorbed): step")
-    o_lat, lse, y = run_step(layer, cfg, case, cache)
-    o_lat = o_lat.view(cfg.batch, n_q, cfg.n_heads, cfg.d_latent).cpu().numpy()
-    lse = lse.view(cfg.batch, n_q, cfg.n_heads).cpu().numpy()
-    y = y.view(cfg.batch, n_q, cfg.d_model).cpu().numpy()
-    for b in range(cfg.batch):
-        js = CHUNK_QUERIES
-        assert_rebases(oracle_for(case, b, js[:8], want_p=True, want_y=False), f"v3 chunk b={b}")
-        ref = chunk_oracle(104, True, b)
-        assert_close(o_lat[b][js], ref["o_lat"], cfg, f"o_lat[b={b}] ({len(js)} queries)")
-        assert_close(lse[b][js], ref["lse"], cfg, f"lse[b={b}]")
-        assert_close(y[b][js], ref["y"], cfg, f"y[b={b}]")
-    assert layer.device_error() == 0
+def rebase_jump_from_query(q_lat, q_pe, c, k, scale):
+    """[n, H] rise (log2 units) of the largest score from the first key
+    block to the second, from a query and the rows (the score definition of
+    page "How DeepSeek Rewrote the Transformer", section 03)."""
+    s = (np.einsum("nhc,mc->nhm", q_lat, c[:2 * TILE]) + np.einsum("nhr,mr->nhm", q_pe, k[:2 * TILE])) * scale
+    s = s / np.log(2.0)
+    return s[..., TILE:].max(-1) - s[..., :TILE].max(-1)
+
+
+@pytest.mark.parametrize("idx,seed,checked", [
+    (1, 111, (0, 9, 15)),     # batch 16 x 4096 contiguous, one query token
+    (2, 112, None),           # batch 64 paged, 512..16384 cached tokens (shortest, median, longest checked)
+    (4, 114, (0, 1)),         # 2 x (4096 + 1024-token causal chunk), sampled queries of both sequences
+])
+def test_rebase_attention_given_query(idx, seed, checked):
+    """mla_attention alone, on the rebase rows, with the query of every
+    checked row taken from the oracle's query path and rounded to bf16 (the
+    interface's query type): both sides see the same query and rows, so the
+    comparison isolates the attention kernels (split, rebase, merge)."""
+    cfg = config(idx)
+    B, n_q, H, R, L = cfg.batch, cfg.n_q, cfg.n_heads, cfg.row, cfg.d_latent
+    rng = np.random.default_rng(seed)
+    W = make_weights(cfg, np.random.default_rng(seed))
+    cached = make_lengths(cfg, rng)
+    kv = cached + n_q
+    rows = make_rows(cfg, kv, rng, quiet_then_loud)       # every visible row, the new tokens' included
+    x_new = make_x(cfg, (B, n_q, cfg.d_model), rng)
+    if checked is None:
+        order = np.argsort(cached)
+        checked = (int(order[0]), int(order[B // 2]), int(order[-1]))
+    js = CHUNK_QUERIES if n_q > 1 else np.array([0])
+    uqk, _ = OA.merged_weights(W, want_uvo=False)
+    q = np.zeros((B, n_q, H, R), np.float32)
+    qr = {}
+    for b in checked:
+        q_lat, q_pe = OA.query_latent(W, uqk, x_new[b][js], cached[b] + js, cfg.rope_base)
+        q_lat, q_pe = round_bf16(q_lat.astype(np.float32)), round_bf16(q_pe.astype(np.float32))
+        q[b, js, :, :L], q[b, js, :, L:] = q_lat, q_pe
+        qr[b] = (q_lat.astype(np.float64), q_pe.astype(np.float64))
+        jump = rebase_jump_from_query(qr[b][0], qr[b][1], rows[b][:, :L], rows[b][:, L:], cfg.softmax_scale)
+        frac = (jump > SLACK_LOG2).mean(-1)
+        print(f"[rebase] {cfg.name} b={b}: heads rebasing after the first key block per query: min {frac.min():.3f}",
+              flush=True)
+        assert (frac > 0.5).all()
+    assert_first_segment_spans_two_blocks(kv, n_q)
+    if cfg.paged:
+        table, n_pages = make_page_table(kv, cfg.page_size, rng)
+        cache, _ = paged_cache(cfg, rows, table, n_pages, kv)
+    else:
+        cache, _ = contiguous_cache(cfg, rows, int(kv.max()))
+    dims = dims_of(cfg)
+    ws = torch.zeros(mla.mla_workspace_size(dims, B, n_q), dtype=torch.uint8, device=DEV)
+    qd = torch.from_numpy(q.reshape(B * n_q, H, R)).to(DEV).to(torch.bfloat16)
+    o_lat = Guarded(B * n_q, H, L)
+    lse = Guarded(B * n_q, H)
+    note(f"rebase attention {cfg.name}")
+    mla.mla_attention(dims, qd, i32(kv), B, n_q, cache, o_lat.t, lse.t, ws)
+    torch.cuda.synchronize()
+    o_lat.check("o_lat")
+    lse.check("lse")
+    assert mla.mla_read_device_error(ws) == 0
+    og = o_lat.t.view(B, n_q, H, L).cpu().numpy()
+    lg = lse.t.view(B, n_q, H).cpu().numpy()
+    for b in checked:
+        ref = OA.attention(qr[b][0], qr[b][1], rows[b][:, :L], rows[b][:, L:], cached[b] + js, cfg.softmax_scale)
+        assert_close(og[b][js], ref["o_lat"], cfg, f"o_lat[b={b}, len={kv[b]}] ({len(js)} queries)", stress=True)
+        assert_close(lg[b][js], ref["lse"], cfg, f"lse[b={b}]", stress=True)
 
 
 def test_rebase_v3_chunk_expanded_prefill():
@@ -164,8 +217,8 @@ def test_rebase_v3_chunk_expanded_prefill():
         js = CHUNK_QUERIES
         assert_rebases(oracle_for(case, b, js[:8], want_p=True, want_y=False), f"v3 prefill b={b}")
         ref = chunk_oracle(104, True, b)
-        assert_close(yy[b][js], ref["y"], cfg, f"y[b={b}] ({len(js)} queries)")
-        assert_close(ll[b][js], ref["lse"], cfg, f"lse[b={b}]")
+        assert_close(yy[b][js], ref["y"], cfg, f"y[b={b}] ({len(js)} queries)", stress=True)
+        assert_close(ll[b][js], ref["lse"], cfg, f"lse[b={b}]", stress=True)
     assert layer.prefill_error() == 0
 
 
@@ -201,7 +254,7 @@ def test_f32_multi_block(lengths, n_q, loud):
         ref = oracle_for(case, b, want_p=loud)
         if loud:
             assert_rebases(ref, f"f32 b={b}")
-        assert_close(o_lat[b], ref["o_lat"], cfg, f"o_lat[b={b}]")
-        assert_close(lse[b], ref["lse"], cfg, f"lse[b={b}]")
-        assert_close(y[b], ref["y"], cfg, f"y[b={b}]")
+        assert_close(o_lat[b], ref["o_lat"], cfg, f"o_lat[b={b}]", stress=True)
+        assert_close(lse[b], ref["lse"], cfg, f"lse[b={b}]", stress=True)
+        assert_close(y[b], ref["y"], cfg, f"y[b={b}]", stress=True)
     assert layer.device_error() == 0
