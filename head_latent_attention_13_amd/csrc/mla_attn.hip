@@ -186,13 +186,16 @@ using CfgF32 = AttnCfg<float, 32, 1, 32, 8, 3>;
 constexpr float kRescaleSlack = 8.0f;
 
 // 16-byte-chunk swizzle inside a 128-byte block row: logical chunk c of
-// tile row r sits at chunk c ^ swz(r).  Rows 128 B apart alternate between
-// the two halves of the 64 banks.  swz permutes the 8 same-parity rows of a
-// 16-row group onto 8 distinct chunks (a 16-lane ds_read_b128 pass of the
-// score phase is conflict-free), and rows r, r+2 (r = 0 mod 4) differ in
-// bit 2, so the 4-row x 32-byte footprint of a transposing PV read never
-// puts two rows on the same banks.
-__device__ inline int swz(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
+// tile row r sits at chunk c ^ swz(r).  Measured on gfx950 (8 waves per CU,
+// ds_read_b128 of a 16x16x32 or 32x32x16 fragment: 16 consecutive rows, one
+// logical chunk per 16 lanes): swz(r) = r & 7 reads at 252 B/clk per CU, the
+// LDS peak, while a swizzle that spreads the 16 rows over the two bank
+// halves by row parity ((r >> 1) & 1 in bit 2) conflicts two ways (135
+// B/clk).  The transposing PV reads run at ~87 B/clk under either.
+__device__ inline int swz(int r) { return r & 7; }
+
+// Byte offset of logical chunk c of row r in a 128-byte-row block.
+__device__ inline int tile_chunk(int r, int c) { return r * 128 + 16 * (c ^ swz(r)); }
 
 // Byte offset of element e of tile row r in an LDS stage.
 template <class C>
@@ -225,6 +228,20 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) 
   return __builtin_amdgcn_make_buffer_rsrc(b, (short)0, __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
+// Buffer-load DMA of this lane's 16 bytes of column blocks KK .. N-1 of a
+// tile (block kk lands 4 KB further in LDS and starts 128 bytes further in
+// the row).  The 128-byte step goes in the scalar offset: the instruction's
+// immediate offset would move the LDS destination as well, and a per-block
+// vector offset costs a register per block.
+template <int KK, int N, int CP>
+__device__ inline void dma_column_blocks(__amdgpu_buffer_rsrc_t rsrc, unsigned char* stage, int wave, int dma_off) {
+  if constexpr (KK < N) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, MLA_LDS_PTR(stage + (wave + 4 * KK) * 1024), 16, dma_off,
+                                             KK * 128, 0, CP);
+    dma_column_blocks<KK + 1, N, CP>(rsrc, stage, wave, dma_off);
+  }
+}
+
 // DMA one 32-row tile into an LDS stage with buffer loads whose record
 // count is the tile's visible bytes: rows at or past `vis`, a page id
 // outside the pool (which also raises error bit 2), and a tile past the end
@@ -255,17 +272,7 @@ __device__ inline void issue_tile(const AttnArgs& a, unsigned char* stage, int b
     // heads in one work-group: C::CNT) the loads are non-temporal (cache
     // policy 2); with several query tokens per sequence the tiles are
     // re-read by the other streams and stay cacheable.
-    if constexpr (C::CNT) {
-#pragma unroll
-      for (int kk = 0; kk < C::NINST / C::NW; ++kk)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, MLA_LDS_PTR(stage + (wave + 4 * kk) * 1024), 16,
-                                                 dma_off + kk * 128, 0, 0, 2);
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < C::NINST / C::NW; ++kk)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, MLA_LDS_PTR(stage + (wave + 4 * kk) * 1024), 16,
-                                                 dma_off + kk * 128, 0, 0, 0);
-    }
+    dma_column_blocks<0, C::NINST / C::NW, C::CNT ? 2 : 0>(rsrc, stage, wave, dma_off);
   } else {
     // row-major rows; 16-byte chunk p of the tile goes to LDS byte 16 p
 #pragma unroll
@@ -543,8 +550,8 @@ __global__ __launch_bounds__(C::NTHR, 1) void attn_split_kernel(AttnArgs a) {
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
-        tr_base[t][h2] = 2 * wave * C::BLOCK_BYTES + (8 * (g >> 1) + 4 * h2 + (sl >> 2)) * 128 +
-                         64 * (t ^ ((sl >> 3) & 1)) + 16 * (c_low ^ (2 * (g >> 1) + h2)) + 8 * (sl & 1);
+        tr_base[t][h2] = 2 * wave * C::BLOCK_BYTES + tile_chunk(8 * (g >> 1) + 4 * h2 + (sl >> 2), 4 * t + c_low) +
+                         8 * (sl & 1);
   }
 
   constexpr int n_loads = C::NINST / C::NW;  // DMA instructions per tile and wave
@@ -1138,8 +1145,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillArgs a) {
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
-        trb[tt][h2] = (4 * hi + 8 * h2 + (sl >> 2)) * 128 + 64 * (tt ^ ((sl >> 3) & 1)) +
-                      16 * (c_low ^ (hi + 2 * h2)) + 8 * (sl & 1);
+        trb[tt][h2] = tile_chunk(4 * hi + 8 * h2 + (sl >> 2), 4 * tt + c_low) + 8 * (sl & 1);
   }
 
   issue(0, smem);
