@@ -5,7 +5,8 @@ include/mla.h); this package is its thin ctypes binding plus a small helper
 that owns the device buffers of one layer (``MLALayer``).
 """
 from ._lib import (MLA_BF16, MLA_F32, MLA_WEIGHTS_FACTORED, MLA_WEIGHTS_MERGED, RAW_WEIGHT_NAMES, Cache, MLAError, EXPORTED, LIB_PATH, load, make_dims,
-                   mla_absorb_weights, mla_absorbed_layout, mla_attention, mla_compress_append, mla_decode,
+                   mla_absorb_weights, mla_absorbed_layout, mla_attention, mla_attention_noalloc, mla_compress_append,
+                   mla_decode,
                    mla_dims, mla_out_proj, mla_prefill_expanded, mla_prefill_workspace_size, mla_q_proj,
                    mla_prefill_workspace_check, mla_read_device_error, mla_version, mla_workspace_check,
                    mla_workspace_size)
@@ -13,7 +14,8 @@ from .layer import MLALayer
 
 __all__ = [
     "MLA_BF16", "MLA_F32", "MLA_WEIGHTS_FACTORED", "MLA_WEIGHTS_MERGED", "RAW_WEIGHT_NAMES", "Cache", "MLAError", "EXPORTED", "LIB_PATH", "load", "make_dims",
-    "mla_absorb_weights", "mla_absorbed_layout", "mla_attention", "mla_compress_append", "mla_decode",
+    "mla_absorb_weights", "mla_absorbed_layout", "mla_attention", "mla_attention_noalloc", "mla_compress_append",
+    "mla_decode",
     "mla_dims", "mla_out_proj", "mla_prefill_expanded", "mla_prefill_workspace_size", "mla_q_proj",
     "mla_prefill_workspace_check", "mla_read_device_error", "mla_version", "mla_workspace_check",
     "mla_workspace_size",

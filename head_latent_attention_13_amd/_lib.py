@@ -75,6 +75,9 @@ _SIGS = {
     "mla_attention": (ctypes.c_int32, [ctypes.POINTER(mla_dims), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                        ctypes.c_int32, ctypes.POINTER(mla_cache), ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "mla_attention_noalloc": (ctypes.c_int32, [ctypes.POINTER(mla_dims), ctypes.c_void_p, ctypes.c_void_p,
+                                               ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(mla_cache),
+                                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "mla_decode": (ctypes.c_int32, [ctypes.POINTER(mla_dims), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                     ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(mla_cache), ctypes.c_void_p,
                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
@@ -209,6 +212,13 @@ def mla_attention(dims, q, kv_len, batch, n_q, cache: Cache, o_lat, lse, workspa
     _check("mla_attention", load().mla_attention(ctypes.byref(dims), _ptr(q), _ptr(kv_len), batch, n_q,
                                                  ctypes.byref(cc), _ptr(o_lat), _ptr(lse), _ptr(workspace),
                                                  _nbytes(workspace), _stream(stream)))
+
+
+def mla_attention_noalloc(dims, q, kv_len, batch, n_q, cache: Cache, o_lat, lse, dev_err=None, stream=None):
+    cc = cache.c()
+    _check("mla_attention_noalloc", load().mla_attention_noalloc(ctypes.byref(dims), _ptr(q), _ptr(kv_len), batch,
+                                                                 n_q, ctypes.byref(cc), _ptr(o_lat), _ptr(lse),
+                                                                 _ptr(dev_err), _stream(stream)))
 
 
 def mla_decode(dims, absorbed, x, kv_len, batch, n_q, cache: Cache, o_lat, lse, workspace, stream=None):

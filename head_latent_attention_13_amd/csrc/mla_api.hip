@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/mla.h"
 #include "mla_common.h"
@@ -306,7 +307,8 @@ mla_status q_proj_impl(const mla_dims* d, const WsLayout& W, const unsigned char
 }
 
 mla_status attention_impl(const mla_dims* d, const WsLayout& W, const void* q, const int32_t* kv_len, int batch,
-                          int n_q, const mla_cache* c, float* o_lat, float* lse, unsigned char* ws, hipStream_t s) {
+                          int n_q, const mla_cache* c, float* o_lat, float* lse, unsigned char* ws, hipStream_t s,
+                          int32_t* err = nullptr) {
   AttnArgs a{};
   a.q = q;
   a.pool = c->pool;
@@ -326,7 +328,7 @@ mla_status attention_impl(const mla_dims* d, const WsLayout& W, const void* q, c
   a.lse = lse;
   a.part_o = reinterpret_cast<float*>(ws + W.attn_o);
   a.part_lse = reinterpret_cast<float*>(ws + W.attn_lse);
-  a.err = reinterpret_cast<int32_t*>(ws + W.err);
+  a.err = err ? err : reinterpret_cast<int32_t*>(ws + W.err);
   a.scale_log2 = scale_of(d) * 1.4426950408889634f;
   a.G = W.G;
   hipError_t e = launch_attention(a, is_bf16(d), s);
@@ -532,6 +534,80 @@ mla_status mla_attention(const mla_dims* d, const void* q, const int32_t* kv_len
   if ((st = check_ws(W, workspace, ws_bytes))) return st;
   return attention_impl(d, W, q, kv_len, batch, n_q, cache, o_lat, lse, reinterpret_cast<unsigned char*>(workspace),
                         reinterpret_cast<hipStream_t>(stream));
+}
+
+// ------------------------------------------------ no-allocation variant ----
+// The device scratch of mla_attention_noalloc: plan records, split partials
+// and, when the caller passes no error word, a device error word.  One copy
+// per GPU, held from the library's first use of it on that GPU until the
+// process ends.  In host code `scratch` names a host-side stand-in: kernels
+// and copies take the device address that hipGetSymbolAddress returns for
+// the current device (g_scratch_dev), never the array's name.
+constexpr size_t kScratchBytes = (size_t)96 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+unsigned char* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of this GPU's scratch, looked up once per device.
+mla_status scratch_address(unsigned char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MLA_ERR_UNSUPPORTED, "device %d: the scratch table covers %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr || !aligned(ptr, 256)) return fail(MLA_ERR_HIP, "scratch address %p is not 256-byte aligned", ptr);
+    g_scratch_dev[dev] = reinterpret_cast<unsigned char*>(ptr);
+  }
+  *out = g_scratch_dev[dev];
+  return MLA_OK;
+}
+
+// Attention regions inside the scratch for U (sequence, head group) units
+// and G split work-groups: error word | plan records | partial O | partial lse.
+size_t scratch_layout(const mla_dims* d, size_t U, int G, WsLayout* W) {
+  const int HG = attn_head_group(is_bf16(d));
+  const size_t slots = (size_t)G + U;
+  size_t o = 0;
+  W->err = o; o = align256(o + 256);
+  W->tile_off = o; o = align256(o + attn_sched_ints((int)U, G) * 4);
+  W->attn_o = o; o = align256(o + slots * HG * d->d_latent * 4);
+  W->attn_lse = o; o = align256(o + slots * HG * 4);
+  W->G = G;
+  return o;
+}
+}  // namespace
+
+mla_status mla_attention_noalloc(const mla_dims* d, const void* q, const int32_t* kv_len, int32_t batch, int32_t n_q,
+                                 const mla_cache* cache, float* o_lat, float* lse, int32_t* dev_err, void* stream) {
+  mla_status st = check_common(d, nullptr, batch, n_q);
+  if (st) return st;
+  if ((st = check_attn_dims(d))) return st;
+  if (!q || !kv_len || !o_lat) return fail(MLA_ERR_INVALID_ARG, "q, kv_len and o_lat must be non-NULL");
+  if (!aligned(q, 16) || !aligned(o_lat, 16) || (lse && !aligned(lse, 4)) || (dev_err && !aligned(dev_err, 4)))
+    return fail(MLA_ERR_INVALID_ARG, "q and o_lat must be 16-byte aligned, lse and dev_err 4-byte aligned");
+  if ((st = check_cache(d, cache, batch))) return st;
+  const int HG = attn_head_group(is_bf16(d));
+  const size_t U = (size_t)batch * n_q * ((d->n_heads + HG - 1) / HG);
+  // as many split work-groups as there are CUs, fewer when the partials of
+  // that many would not fit the scratch, never fewer than 8
+  WsLayout W{};
+  int G = std::min(device_cus(), 1024);
+  while (G > 8 && (U > (size_t)(1 << 24) || scratch_layout(d, U, G, &W) > kScratchBytes)) --G;
+  if (U > (size_t)(1 << 24) || scratch_layout(d, U, G, &W) > kScratchBytes)
+    return fail(MLA_ERR_WORKSPACE, "%zu (sequence, head group) units need %zu scratch bytes, the maximum is %zu",
+                U, scratch_layout(d, U, 8, &W), kScratchBytes);
+  W.plans_ok = true;
+  unsigned char* ws = nullptr;
+  if ((st = scratch_address(&ws))) return st;
+  return attention_impl(d, W, q, kv_len, batch, n_q, cache, o_lat, lse, ws, reinterpret_cast<hipStream_t>(stream),
+                        dev_err);
 }
 
 mla_status mla_decode(const mla_dims* d, const void* absorbed, const void* x, const int32_t* kv_len, int32_t batch,

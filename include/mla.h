@@ -230,6 +230,25 @@ mla_status mla_attention(const mla_dims *dims, const void *q, const int32_t *kv_
                          const mla_cache *cache, float *o_lat, float *lse, void *workspace, size_t ws_bytes,
                          void *stream);
 
+/* mla_attention for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels with the same arguments, except that the plan records
+ * and split partials live in a library-owned scratch array of 96 MiB per
+ * GPU (held from its first use on that GPU until the process ends) instead
+ * of a caller workspace.  Nothing is allocated: no hipMalloc, hipFree or
+ * allocating library call.
+ *   dev_err  device int32, or NULL: the error bits of mla_read_device_error
+ *            are OR-ed into it (the caller zeroes it); with NULL they go to
+ *            a word in the scratch that nobody reads.
+ * The split uses one work-group per CU, or fewer when the partials of that
+ * many would not fit the scratch (batch * n_q * ceil(H / 128) above 127 at
+ * d_latent 512); when not even 8 fit, returns MLA_ERR_WORKSPACE.  Every
+ * call on a GPU shares that GPU's scratch: calls that overlap on one GPU
+ * (two streams, two threads) race and must be serialised by the caller. */
+mla_status mla_attention_noalloc(const mla_dims *dims, const void *q, const int32_t *kv_len, int32_t batch,
+                                 int32_t n_q, const mla_cache *cache, float *o_lat, float *lse, int32_t *dev_err,
+                                 void *stream);
+
 /* mla_q_proj followed by mla_attention, with q kept in the workspace. */
 mla_status mla_decode(const mla_dims *dims, const void *absorbed, const void *x, const int32_t *kv_len,
                       int32_t batch, int32_t n_q, const mla_cache *cache, float *o_lat, float *lse,
