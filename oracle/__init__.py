@@ -15,15 +15,20 @@ Modules
               pinned to ``expanded`` by the tests and serves as the cheaper
               reference at sizes where expanding every latent is too slow.
 ``rope``      the rotary position embedding used on the decoupled key/query.
+``fp8``       E4M3 codes with one power-of-two scale per cache row (the
+              FP8 latent cache): encode / decode from the format
+              definition, the row quantiser and its inverse.
 
 Pins (see ``tests/test_oracle_pins.py``): equality with textbook MHA and with
 ``torch.nn.functional.scaled_dot_product_attention`` when RoPE is removed,
 absorbed = expanded, softmax invariants, a pure-Python brute force on the
 tiny config, decode = last row of full causal attention, RoPE invariants and
-the byte-count closed forms the pages print.
+the byte-count closed forms the pages print; ``fp8`` against
+torch.float8_e4m3fn casts, a brute-force scale search and the rounding
+error bounds (``tests/test_oracle_fp8.py``).
 
 Parity unpinned (conventions the pages leave open and both sides adopt):
 the RoPE pair layout and frequencies, the source of the query's RoPE part
 (the query latent), and the softmax scale 1/sqrt(d_nope + d_rope).
 """
-from . import rope, expanded, absorbed, accounting  # noqa: F401
+from . import rope, expanded, absorbed, accounting, fp8  # noqa: F401
