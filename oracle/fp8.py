@@ -22,7 +22,9 @@ larger magnitude has no finite code and becomes NaN (sign kept).
 
 Row quantiser: scale s = 2^k with k the smallest integer such that
 amax <= 448 * 2^k (amax = the largest |value| of the fp32 row; s = 1 for a
-row of zeros), then code = encode(value / s).  Because s is a power of two
+row of zeros), but no smaller than -126 so that s and 1/s are normal fp32
+numbers (rows below 448 * 2^-126 keep that scale and round towards
+zero), then code = encode(value / s).  Because s is a power of two
 the division is exact, every code * s is exactly representable in bf16,
 and the scaled row's largest magnitude lies in (224, 448].  k is read off
 the binary exponent of the fp32 amax, amax = f * 2^E with f in [0.5, 1):
@@ -73,11 +75,11 @@ def encode(x) -> np.ndarray:
 
 
 def row_scale_exponents(rows) -> np.ndarray:
-    """k per row: the smallest integer with amax <= 448 * 2^k (0 for zero rows)."""
+    """k per row: the smallest integer >= -126 with amax <= 448 * 2^k (0 for zero rows)."""
     r = np.asarray(rows, dtype=np.float32)
     amax = np.max(np.abs(r), axis=-1).astype(np.float64)
     f, E = np.frexp(amax)
-    k = np.where(f <= 0.875, E - 9, E - 8)
+    k = np.maximum(np.where(f <= 0.875, E - 9, E - 8), -126)
     return np.where(amax == 0, 0, k).astype(np.int64)
 
 

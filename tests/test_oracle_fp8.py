@@ -7,8 +7,8 @@ Pins:
     every exact midpoint between neighbouring codes (ties), the subnormal
     range, the overflow edge, signed zeros, inf / NaN and random values;
   * encode(decode(c)) == c for every finite code (the grid is exact);
-  * the row scale exponent is the smallest k with amax <= 448 * 2^k, found
-    by brute force over k;
+  * the row scale exponent is the smallest k >= -126 with amax <= 448 * 2^k,
+    found by brute force over k;
   * round-to-nearest error bounds of the quantised rows, and the scaled
     row's largest magnitude in (224, 448] before rounding.
 Planted slips in the oracle (bias, rounding mode, subnormal spacing, scale
@@ -72,6 +72,8 @@ def pin_scale_exponent(F):
     rows[1, 3] = np.float32(448.0)       # amax exactly 448 * 2^0
     rows[2, :] = np.float32(448.0 * 2.0 ** -5)
     rows[3, 0] = np.float32(np.nextafter(np.float32(448.0), np.float32(1e9)))
+    rows[4, :] = np.float32(3e-38)       # below 448 * 2^-126: the exponent stops at -126
+    rows[5, :] = np.float32(448.0 * 2.0 ** -126)
     k = F.row_scale_exponents(rows)
     bad = 0
     for r, kk in zip(rows, k):
@@ -79,7 +81,7 @@ def pin_scale_exponent(F):
         if amax == 0:
             bad += kk != 0
             continue
-        ks = [j for j in range(-160, 160) if amax <= 448.0 * 2.0 ** j]
+        ks = [j for j in range(-126, 160) if amax <= 448.0 * 2.0 ** j]
         bad += kk != min(ks)
     return int(bad)
 
@@ -132,8 +134,9 @@ MUTATIONS = [
     ("q = np.round(fin / step)", "q = np.floor(fin / step + 0.5)"),                    # ties away
     ("e_unb = np.maximum(E - 1, -6)", "e_unb = np.maximum(E - 1, -7)"),                # subnormal spacing
     ("overflow = (a > 464.0)", "overflow = (a >= 464.0)"),                             # overflow edge
-    ("k = np.where(f <= 0.875, E - 9, E - 8)", "k = np.where(f < 0.875, E - 9, E - 8)"),  # scale at 448 * 2^k
-    ("k = np.where(f <= 0.875, E - 9, E - 8)", "k = E - 8"),                           # one binade too coarse
+    ("np.where(f <= 0.875, E - 9, E - 8)", "np.where(f < 0.875, E - 9, E - 8)"),      # scale at 448 * 2^k
+    ("np.where(f <= 0.875, E - 9, E - 8)", "(E - 8)"),                                 # one binade too coarse
+    ("np.where(f <= 0.875, E - 9, E - 8), -126)", "np.where(f <= 0.875, E - 9, E - 8), -149)"),  # no floor
     ("return decode(codes) * np.asarray(scales", "return decode(codes) / np.asarray(scales"),  # inverse scale
 ]
 
