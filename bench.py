@@ -52,6 +52,8 @@ def parse():
     p.add_argument("--prefill", choices=("absorbed", "expanded"), default="absorbed",
                    help="expanded: the step is append + mla_prefill_expanded (factored weights, contiguous cache; "
                         "the V3 chunked-prefill workload)")
+    p.add_argument("--cache", choices=("dtype", "e4m3"), default="dtype",
+                   help="latent cache rows: the layer dtype, or E4M3 codes with one scale per row (bf16 layers)")
     p.add_argument("--graph", action="store_true",
                    help="replay each step from a HIP graph captured once per input copy")
     p.add_argument("--copies", type=int, default=4,
@@ -206,6 +208,10 @@ def main():
             print("--prefill expanded needs a contiguous cache", file=sys.stderr)
             sys.exit(2)
         args.form = "factored"
+    e4 = args.cache == "e4m3"
+    if e4 and (cfg.dtype != "bf16" or args.prefill == "expanded"):
+        print("--cache e4m3 needs a bf16 layer and the absorbed path", file=sys.stderr)
+        sys.exit(2)
     case = make_case(cfg, args.config, history="rows")
     B, n_q, H, R = cfg.batch, cfg.n_q, cfg.n_heads, cfg.row
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
@@ -245,16 +251,42 @@ def main():
         for b in range(B):
             pool[b, :len(case.rows[b])] = devt(case.rows[b])
         cache = mla.Cache(pool=pool, s_max=s_max)
+    scales = None
+    if e4:
+        # the same history rows, quantised by the library into an E4M3 cache
+        # of the same layout (one sequence at a time, through its row of the
+        # page table)
+        e4pool = torch.zeros(pool.shape, dtype=torch.uint8, device="cuda")
+        scales = torch.zeros(pool.shape[:2], dtype=torch.float32, device="cuda")
+        for b in range(B):
+            S = len(case.rows[b])
+            if S == 0:
+                continue
+            rows32 = torch.from_numpy(np.ascontiguousarray(case.rows[b], np.float32)).cuda()
+            if cfg.paged:
+                one = mla.Cache(pool=e4pool, page_table=table[b:b + 1].contiguous(), page_size=P, n_pages=case.n_pages,
+                                max_pages_per_seq=case.page_table.shape[1], scales=scales)
+            else:
+                one = mla.Cache(pool=e4pool[b:b + 1], s_max=s_max, scales=scales[b:b + 1])
+            layer.store_rows(rows32, torch.zeros(1, dtype=torch.int32, device="cuda"), 1, S, one)
+        torch.cuda.synchronize()
+        assert layer.device_error() == 0
+        pool = e4pool
+        cache = (mla.Cache(pool=pool, page_table=table, page_size=P, n_pages=case.n_pages,
+                           max_pages_per_seq=case.page_table.shape[1], scales=scales) if cfg.paged
+                 else mla.Cache(pool=pool, s_max=s_max, scales=scales))
     x = devt(case.x_new.reshape(B * n_q, cfg.d_model))
     pos = torch.from_numpy(case.cached.astype(np.int32)).cuda()
     kv = torch.from_numpy(kv_len.astype(np.int32)).cuda()
     # copy j of every input: step k runs on copy k % NC
     if cfg.paged:
         caches = [cache] + [mla.Cache(pool=pool.clone(), page_table=table.clone(), page_size=cache.page_size,
-                                      n_pages=cache.n_pages, max_pages_per_seq=cache.max_pages_per_seq)
+                                      n_pages=cache.n_pages, max_pages_per_seq=cache.max_pages_per_seq,
+                                      scales=None if scales is None else scales.clone())
                             for _ in range(NC - 1)]
     else:
-        caches = [cache] + [mla.Cache(pool=pool.clone(), s_max=cache.s_max) for _ in range(NC - 1)]
+        caches = [cache] + [mla.Cache(pool=pool.clone(), s_max=cache.s_max,
+                                      scales=None if scales is None else scales.clone()) for _ in range(NC - 1)]
     xs = [x] + [x.clone() for _ in range(NC - 1)]
     poss = [pos] + [pos.clone() for _ in range(NC - 1)]
     kvs = [kv] + [kv.clone() for _ in range(NC - 1)]
@@ -336,9 +368,10 @@ def main():
     rows_visible = int(kv_len.sum())
     pairs = int(sum(int(c) * n_q + n_q * (n_q + 1) // 2 for c in case.cached))  # unmasked (query, key) pairs
     _, wbytes, _ = mla.mla_absorbed_layout(dims)
-    cache_bytes = (rows_visible if n_q == 1 else int(B * (int(case.cached.max()) + n_q))) * R * eb
+    row_bytes = R + 4 if e4 else R * eb  # E4M3: one byte per element plus the row's fp32 scale
+    cache_bytes = (rows_visible if n_q == 1 else int(B * (int(case.cached.max()) + n_q))) * row_bytes
     algo = {
-        "mla_compress_append": {"bytes": wbytes[0] + M * cfg.d_model * eb + M * R * eb,
+        "mla_compress_append": {"bytes": wbytes[0] + M * cfg.d_model * eb + M * row_bytes,
                                 "flops": 2 * M * cfg.d_model * R},
         "mla_q_proj": {"bytes": wbytes[1] + wbytes[2] + M * cfg.d_model * eb + M * H * R * eb,
                        "flops": 2 * M * cfg.d_model * cfg.d_q_latent + 2 * M * cfg.d_q_latent * H * R},
@@ -384,7 +417,8 @@ def main():
                       "roofline_frac": round((t_hbm if bound == "hbm" else t_mfma) / t, 4)}
     dom = "mla_prefill_expanded" if expanded else ROOFLINE_CALL
     d = kernels[dom]
-    traffic = measured_traffic(dom, cfg.name)
+    workload = cfg.name + ("_e4m3" if e4 else "")
+    traffic = measured_traffic(dom, workload)
     if d["bound"] == "hbm":
         roofline = {"bound": "hbm", "achieved": d["GB_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(d["GB_s"] / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom,
@@ -409,10 +443,11 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
         "data": "synthetic (seeded; random-init weights of the DeepSeek-V2 layer shape)",
-        "config": {"workload": cfg.name, "batch": B, "cached_tokens": (list(cfg.cached) if isinstance(cfg.cached, tuple)
+        "config": {"workload": workload, "batch": B, "cached_tokens": (list(cfg.cached) if isinstance(cfg.cached, tuple)
                                                                       else int(cfg.cached)),
                    "new_tokens": n_q, "heads": H, "d_latent": cfg.d_latent, "d_rope": cfg.d_rope,
                    "d_model": cfg.d_model, "cache": "paged" if cfg.paged else "contiguous",
+                   "cache_rows": "e4m3 + fp32 scale per row" if e4 else cfg.dtype,
                    "weights": args.form, "prefill": args.prefill,
                    "launch": "HIP graph per step" if args.graph else "stream"},
         "roofline": roofline,
@@ -421,11 +456,12 @@ def main():
         "attention_mfma_pct": round(100 * att["mfma_frac"], 2),
         "attention_roofline_frac": att["roofline_frac"],
         # measured from the allocation (paged pools round up to whole pages)
-        "kv_bytes_per_token_per_layer": round(pool.numel() * pool.element_size() / int(kv_len.sum()), 1),
+        "kv_bytes_per_token_per_layer": round((pool.numel() * pool.element_size()
+                                               + (0 if scales is None else scales.numel() * 4)) / int(kv_len.sum()), 1),
         "kernels": kernels,
         # rocprofv3 counters (SQ_INSTS_VALU_MFMA_MOPS_BF16 calibrated on a product of known size,
         # SQ_VALU_MFMA_BUSY_CYCLES / GRBM_GUI_ACTIVE), when taken on these kernel sources
-        "mfma_counters": (measured_mfma(cfg.name) if args.form == "merged" and not expanded else None),
+        "mfma_counters": (measured_mfma(workload) if args.form == "merged" and not expanded else None),
         "absorb_ms_once": round(absorb_ms, 3),
     }
     if not args.no_cpu_baseline:

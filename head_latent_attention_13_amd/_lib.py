@@ -26,6 +26,9 @@ MLA_WEIGHTS_FACTORED = 1
 RAW_WEIGHT_NAMES = ("W_DQ", "W_UQ", "W_QR", "W_DKV", "W_KR", "W_UK", "W_UV", "W_O")
 
 
+MLA_ROWS_DTYPE, MLA_ROWS_E4M3 = 0, 1
+
+
 class MLAError(RuntimeError):
     def __init__(self, fn: str, status: int, msg: str):
         super().__init__(f"{fn} failed: {msg} ({status})")
@@ -45,7 +48,8 @@ class mla_raw_weights(ctypes.Structure):
 
 class mla_cache(ctypes.Structure):
     _fields_ = [("pool", ctypes.c_void_p), ("page_table", ctypes.c_void_p), ("page_size", ctypes.c_int32),
-                ("n_pages", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32), ("s_max", ctypes.c_int32)]
+                ("n_pages", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32), ("s_max", ctypes.c_int32),
+                ("row_format", ctypes.c_int32), ("scales", ctypes.c_void_p)]
 
 
 _lib = None
@@ -69,6 +73,9 @@ _SIGS = {
                                              ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                              ctypes.POINTER(mla_cache), ctypes.c_void_p, ctypes.c_size_t,
                                              ctypes.c_void_p]),
+    "mla_cache_store_rows": (ctypes.c_int32, [ctypes.POINTER(mla_dims), ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(mla_cache),
+                                              ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "mla_q_proj": (ctypes.c_int32, [ctypes.POINTER(mla_dims), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                     ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                     ctypes.c_size_t, ctypes.c_void_p]),
@@ -135,17 +142,23 @@ def make_dims(d_model, n_heads, d_latent, d_q_latent, d_nope, d_rope, d_v, dtype
 
 @dataclass
 class Cache:
-    """Latent cache: contiguous pool [B, s_max, R] or paged pool [P, page_size, R]."""
+    """Latent cache: contiguous pool [B, s_max, R] or paged pool [P, page_size, R].
+
+    With ``scales`` set the rows are E4M3 codes (uint8 pool) and ``scales``
+    holds one fp32 scale per row slot ([B, s_max] or [P, page_size])."""
     pool: torch.Tensor
     page_table: Optional[torch.Tensor] = None
     page_size: int = 0
     n_pages: int = 0
     max_pages_per_seq: int = 0
     s_max: int = 0
+    scales: Optional[torch.Tensor] = None
 
     def c(self) -> mla_cache:
         return mla_cache(self.pool.data_ptr(), None if self.page_table is None else self.page_table.data_ptr(),
-                         self.page_size, self.n_pages, self.max_pages_per_seq, self.s_max)
+                         self.page_size, self.n_pages, self.max_pages_per_seq, self.s_max,
+                         MLA_ROWS_DTYPE if self.scales is None else MLA_ROWS_E4M3,
+                         None if self.scales is None else self.scales.data_ptr())
 
 
 def mla_version() -> str:
@@ -200,6 +213,13 @@ def mla_compress_append(dims, absorbed, x, pos, batch, n_q, cache: Cache, worksp
     _check("mla_compress_append", load().mla_compress_append(
         ctypes.byref(dims), _ptr(absorbed), _ptr(x), _ptr(pos), batch, n_q, ctypes.byref(cc), _ptr(workspace),
         _nbytes(workspace), _stream(stream)))
+
+
+def mla_cache_store_rows(dims, rows, pos, batch, n_q, cache: Cache, workspace, stream=None):
+    cc = cache.c()
+    _check("mla_cache_store_rows", load().mla_cache_store_rows(ctypes.byref(dims), _ptr(rows), _ptr(pos), batch, n_q,
+                                                               ctypes.byref(cc), _ptr(workspace), _nbytes(workspace),
+                                                               _stream(stream)))
 
 
 def mla_q_proj(dims, absorbed, x, kv_len, batch, n_q, q, workspace, stream=None):

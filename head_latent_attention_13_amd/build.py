@@ -12,7 +12,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmla.so")
-SOURCES = ("mla_api.hip", "mla_gemm.hip", "mla_attn.hip")
+SOURCES = ("mla_api.hip", "mla_gemm.hip", "mla_attn.hip", "mla_cache.hip")
 ARCH = os.environ.get("MLA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

@@ -249,9 +249,44 @@ mla_status check_cache(const mla_dims* d, const mla_cache* c, int batch) {
   } else {
     if (c->s_max <= 0) return fail(MLA_ERR_INVALID_ARG, "contiguous cache needs s_max > 0");
   }
-  (void)d;
+  if (c->row_format != MLA_ROWS_DTYPE && c->row_format != MLA_ROWS_E4M3)
+    return fail(MLA_ERR_INVALID_ARG, "row_format %d", c->row_format);
+  if (c->row_format == MLA_ROWS_E4M3) {
+    if (!is_bf16(d)) return fail(MLA_ERR_UNSUPPORTED, "E4M3 cache rows need a bf16 layer");
+    if (!c->scales || !aligned(c->scales, 4)) return fail(MLA_ERR_INVALID_ARG, "E4M3 cache needs 4-byte aligned scales");
+    if (row_width(d) % 16) return fail(MLA_ERR_UNSUPPORTED, "E4M3 cache rows need R a multiple of 16");
+  }
   (void)batch;
   return MLA_OK;
+}
+
+bool e4m3(const mla_cache* c) { return c->row_format == MLA_ROWS_E4M3; }
+
+// The cache-store arguments for rows [M][R] fp32 at positions pos[b] + t.
+StoreArgs store_args(const mla_dims* d, const mla_cache* c, const float* rows, const int32_t* pos, int M, int n_q,
+                     bool rope, int32_t* err) {
+  StoreArgs a{};
+  a.rows = rows;
+  a.pos = pos;
+  a.M = M;
+  a.n_q = n_q;
+  a.R = row_width(d);
+  a.d_latent = d->d_latent;
+  a.d_rope = d->d_rope;
+  a.rope = rope ? 1 : 0;
+  a.rope_base = d->rope_base;
+  a.format = e4m3(c) ? 1 : 0;
+  a.bf16 = is_bf16(d) ? 1 : 0;
+  a.pool = c->pool;
+  a.scales = c->scales;
+  a.page_table = c->page_table;
+  a.paged = c->page_table != nullptr;
+  a.page_size = c->page_size;
+  a.n_pages = c->n_pages;
+  a.max_pages = c->max_pages_per_seq;
+  a.s_max = c->s_max;
+  a.err = err;
+  return a;
 }
 
 enum { G_APP = 0, G_CQ = 1, G_Q = 2, G_OUT = 3 };
@@ -331,6 +366,8 @@ mla_status attention_impl(const mla_dims* d, const WsLayout& W, const void* q, c
   a.err = err ? err : reinterpret_cast<int32_t*>(ws + W.err);
   a.scale_log2 = scale_of(d) * 1.4426950408889634f;
   a.G = W.G;
+  a.e4m3 = e4m3(c) ? 1 : 0;
+  a.scales = c->scales;
   hipError_t e = launch_attention(a, is_bf16(d), s);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return MLA_OK;
@@ -497,6 +534,18 @@ mla_status mla_compress_append(const mla_dims* d, const void* absorbed, const vo
   const bool bf = is_bf16(d);
   const AbsLayout L = abs_layout(d);
   unsigned char* ws = reinterpret_cast<unsigned char*>(workspace);
+  if (e4m3(cache)) {
+    // E4M3 rows: the GEMM leaves fp32 rows in the q region (unused by an
+    // append), then one wave per row applies RoPE and quantises into the cache
+    float* rows = reinterpret_cast<float*>(ws + W.q);
+    st = run_gemm(W, G_APP, W.g_app, bf, false, x, d->d_model, reinterpret_cast<const unsigned char*>(absorbed) + L.off[0],
+                  ws, base_epi(EPI_F32, rows), s);
+    if (st) return st;
+    hipError_t he = launch_cache_store(store_args(d, cache, rows, pos, batch * n_q, n_q, true,
+                                                  reinterpret_cast<int32_t*>(ws + W.err)), s);
+    if (he != hipSuccess) return hip_fail(he, "cache store launch");
+    return MLA_OK;
+  }
   EpiArgs e = base_epi(EPI_APPEND, nullptr);
   e.d_latent = d->d_latent; e.d_rope = d->d_rope; e.row = row_width(d); e.rope_base = d->rope_base;
   e.n_q = n_q; e.pos = pos;
@@ -506,6 +555,23 @@ mla_status mla_compress_append(const mla_dims* d, const void* absorbed, const vo
   e.err = reinterpret_cast<int32_t*>(ws + W.err);
   return run_gemm(W, G_APP, W.g_app, bf, false, x, d->d_model, reinterpret_cast<const unsigned char*>(absorbed) + L.off[0],
                   ws, e, s);
+}
+
+mla_status mla_cache_store_rows(const mla_dims* d, const float* rows, const int32_t* pos, int32_t batch, int32_t n_q,
+                                const mla_cache* cache, void* workspace, size_t ws_bytes, void* stream) {
+  mla_status st = check_common(d, nullptr, batch, n_q);
+  if (st) return st;
+  if (!rows || !pos) return fail(MLA_ERR_INVALID_ARG, "rows and pos must be non-NULL");
+  if (!aligned(rows, 16)) return fail(MLA_ERR_INVALID_ARG, "rows must be 16-byte aligned");
+  if ((st = check_cache(d, cache, batch))) return st;
+  // only the device error word (the first 256 bytes of any workspace) is used
+  if (!workspace || !aligned(workspace, 256)) return fail(MLA_ERR_INVALID_ARG, "workspace must be non-NULL and 256-byte aligned");
+  if (ws_bytes < 256) return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes < 256 needed", ws_bytes);
+  hipError_t he = launch_cache_store(store_args(d, cache, rows, pos, batch * n_q, n_q, false,
+                                                reinterpret_cast<int32_t*>(workspace)),
+                                     reinterpret_cast<hipStream_t>(stream));
+  if (he != hipSuccess) return hip_fail(he, "cache store launch");
+  return MLA_OK;
 }
 
 mla_status mla_q_proj(const mla_dims* d, const void* absorbed, const void* x, const int32_t* kv_len, int32_t batch,
@@ -685,6 +751,7 @@ mla_status mla_prefill_expanded(const mla_dims* d, const void* absorbed, const v
   if (!aligned(x, 16) || !aligned(y, 16)) return fail(MLA_ERR_INVALID_ARG, "x and y must be 16-byte aligned");
   if ((st = check_cache(d, cache, batch))) return st;
   if (cache->page_table) return fail(MLA_ERR_UNSUPPORTED, "expanded prefill reads a contiguous cache");
+  if (e4m3(cache)) return fail(MLA_ERR_UNSUPPORTED, "expanded prefill reads bf16 cache rows");
   const PfLayout P = pf_fit(d, batch, n_q, cache->s_max, ws_bytes);
   if (!workspace || !aligned(workspace, 256)) return fail(MLA_ERR_INVALID_ARG, "workspace must be non-NULL and 256-byte aligned");
   if (ws_bytes < P.total) return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, P.total);

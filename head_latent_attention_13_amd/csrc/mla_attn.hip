@@ -129,10 +129,13 @@ __device__ inline void o_settle(f32x16 (&O)[NTH][NCT]) {
   }
 }
 
-template <typename T_, int HP_, int NW_, int DL_, int DR_, int NSTAGE_, bool CNT_ = false>
+template <typename T_, int HP_, int NW_, int DL_, int DR_, int NSTAGE_, bool CNT_ = false, bool E4_ = false>
 struct AttnCfg {
   // cache rows read by one stream only: non-temporal tile loads
   static constexpr bool CNT = CNT_;
+  // cache rows are E4M3 codes with per-row scales: tiles are DMA'd into a
+  // two-slot staging ring and converted into the bf16 tile slots
+  static constexpr bool E4 = E4_;
   using T = T_;
   using F = Mfma32<T>;
   static constexpr int HP = HP_, NW = NW_, DL = DL_, DR = DR_, R = DL_ + DR_;
@@ -165,13 +168,24 @@ struct AttnCfg {
   static constexpr int OFF_M = OFF_ALPHA + HP * 4;
   static constexpr int OFF_L = OFF_M + HP * 4;
   static constexpr int OFF_FLAG = OFF_L + HP * 4;
-  static constexpr int LDS_BYTES = OFF_FLAG + NTH * 4;
+  // E4M3 staging slot: TILE rows of R codes, then 256 B of scales (one per
+  // lane of the scale load, rows past the tile read as 0) and 256 B that
+  // the padding load of a wave without a block of its own writes
+  static constexpr int E4_TILE = TILE * R;
+  static constexpr int E4_BLOCKS = E4_TILE / 1024;
+  static constexpr int E4_STAGE = E4_TILE + 512;
+  static constexpr int E4_LOADS = (E4_BLOCKS + 2 + NW - 1) / NW;  // DMA instructions per tile and wave
+  static constexpr int OFF_E4 = (OFF_FLAG + NTH * 4 + 15) & ~15;
+  static constexpr int LDS_BYTES = E4 ? OFF_E4 + 2 * E4_STAGE : OFF_FLAG + NTH * 4;
   static_assert(NTH == NW, "one 32-head tile per wave in the score phase");
   static_assert(R % KB == 0 && TILE % KB == 0, "whole MFMA k-steps");
   static_assert(TILE_BYTES % 1024 == 0 && NINST % NW == 0, "tile must be whole 1 KB DMA blocks per wave");
   static_assert(DL % (NW * 32) == 0, "latent columns must split evenly over waves");
   static_assert(ROW_BYTES % 16 == 0, "rows must be whole 16 B chunks");
   static_assert(!FAST || NINST == 4 * (ROW_CHUNKS / 8), "FAST: 4 DMA blocks per column block");
+  static_assert(!E4 || (FAST && NSTAGE == 2 && E4_TILE % 1024 == 0 && E4_LOADS * NW == E4_BLOCKS + 2),
+                "E4M3: bf16 FAST layout, two bf16 slots, whole 1 KB code blocks plus the scale and padding loads");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
 
 // 128 heads per work-group: 4 waves x 32 heads (score phase), 4 waves x 128
@@ -179,6 +193,8 @@ struct AttnCfg {
 // AGPRs of the four waves.
 using CfgBf16 = AttnCfg<__bf16, 128, 4, 512, 64, 3>;
 using CfgBf16Nt = AttnCfg<__bf16, 128, 4, 512, 64, 3, true>;
+using CfgE4 = AttnCfg<__bf16, 128, 4, 512, 64, 2, false, true>;
+using CfgE4Nt = AttnCfg<__bf16, 128, 4, 512, 64, 2, true, true>;
 using CfgF32 = AttnCfg<float, 32, 1, 32, 8, 3>;
 
 // Softmax statistics are only rebased when a head's running max grows by
@@ -284,6 +300,113 @@ __device__ inline void issue_tile(const AttnArgs& a, unsigned char* stage, int b
   }
 }
 
+// E4M3 cache: DMA one 32-row tile of codes (contiguous R-byte rows, one
+// 1 KB block per load) and its 32 scales into a staging slot.  Wave w takes
+// blocks w, w + NW, ...; the last two load slots are the scales and a
+// padding load into the slot's spare 256 B, so that every wave issues
+// E4_LOADS loads.  Rows at or past `vis`, a page outside the pool (error
+// bit 2) and a dead tile read as zeros, as in issue_tile.
+template <class C>
+__device__ inline void issue_tile_e4(const AttnArgs& a, unsigned char* st, int b, int k, int vis, int wave, int lane,
+                                     bool live) {
+  const int t0 = k * C::TILE;
+  size_t row0 = 0;
+  bool ok = live;
+  if (live) {
+    if (a.paged) {
+      const int pg = MLA_CONST_PTR(a.page_table)[(size_t)b * a.max_pages + t0 / a.page_size];
+      ok = (pg >= 0) && (pg < a.n_pages);
+      if (!ok && lane == 0) atomicOr(a.err, 2);
+      row0 = (size_t)(ok ? pg : 0) * a.page_size + (t0 % a.page_size);
+    } else {
+      row0 = (size_t)b * a.s_max + t0;
+    }
+  }
+  const int rows = ok ? min(max(vis - t0, 0), C::TILE) : 0;
+  const __amdgpu_buffer_rsrc_t rc = make_rsrc(reinterpret_cast<const unsigned char*>(a.pool) + row0 * C::R, rows * C::R);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scales + row0, rows * 4);
+  constexpr int CP = C::CNT ? 2 : 0;
+#pragma unroll
+  for (int i = 0; i < C::E4_LOADS; ++i) {
+    const int j = wave + C::NW * i;  // wave-uniform
+    if (j < C::E4_BLOCKS)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, MLA_LDS_PTR(st + j * 1024), 16, lane * 16, j * 1024, 0, CP);
+    else if (j == C::E4_BLOCKS)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, MLA_LDS_PTR(st + C::E4_TILE), 4, lane * 4, 0, 0, CP);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(g_zero_rows, 0), MLA_LDS_PTR(st + C::E4_TILE + 256), 4, 0, 0,
+                                               0, 0);
+  }
+}
+
+// Converts a staged E4M3 tile into a bf16 tile slot (FAST layout), 16 codes
+// per thread and item; code * scale is exact in
+// bf16 for the power-of-two scales the library writes.  The conversion is
+// v_cvt_scalef32_pk_bf16_fp8 (two codes of the selected 16-bit half, times
+// the fp32 scale, to two bf16), written in one asm block per chunk: the
+// compiler's builtin for it keeps only the first result of each pair (it
+// copies the low bf16 over the high one), while the instruction itself
+// gives the format's value for all 256 codes (checked against
+// torch.float8_e4m3fn on this hardware).  The block's inputs come from LDS
+// loads (waited for by the compiler before the asm) and its trailing
+// s_nop leaves wait states before any consumer of the results.
+// Items k0 .. k0 + N - 1 of this thread: all loaded, then converted.
+template <class C, int N>
+__device__ inline void convert_items_e4(const unsigned char* __restrict__ st, unsigned char* __restrict__ tb, int tid,
+                                        int k0) {
+  constexpr int ITEMS_PER_BLOCK = C::TILE * 4;
+  constexpr int ITEMS = C::E4_TILE / 16;
+  const float* sc = reinterpret_cast<const float*>(st + C::E4_TILE);
+  uint4 w[N];
+  float s[N];
+  int off[N];
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    const int it = min(tid + (k0 + k) * C::NTHR, ITEMS - 1);  // the tail repeats the last item (same value, same place)
+    const int blk = it / ITEMS_PER_BLOCK, rem = it - blk * ITEMS_PER_BLOCK;
+    const int r = rem >> 2, e0 = blk * 64 + (rem & 3) * 16;
+    w[k] = *reinterpret_cast<const uint4*>(st + r * C::R + e0);
+    s[k] = sc[r];
+    off[k] = lds_off<C>(r, e0);
+  }
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    uint32_t o0, o1, o2, o3, o4, o5, o6, o7;
+    asm volatile(
+        "v_cvt_scalef32_pk_bf16_fp8 %0, %8, %12\n\t"
+        "v_cvt_scalef32_pk_bf16_fp8 %1, %8, %12 op_sel:[1,0,0]\n\t"
+        "v_cvt_scalef32_pk_bf16_fp8 %2, %9, %12\n\t"
+        "v_cvt_scalef32_pk_bf16_fp8 %3, %9, %12 op_sel:[1,0,0]\n\t"
+        "v_cvt_scalef32_pk_bf16_fp8 %4, %10, %12\n\t"
+        "v_cvt_scalef32_pk_bf16_fp8 %5, %10, %12 op_sel:[1,0,0]\n\t"
+        "v_cvt_scalef32_pk_bf16_fp8 %6, %11, %12\n\t"
+        "v_cvt_scalef32_pk_bf16_fp8 %7, %11, %12 op_sel:[1,0,0]\n\t"
+        "s_nop 1"
+        : "=&v"(o0), "=&v"(o1), "=&v"(o2), "=&v"(o3), "=&v"(o4), "=&v"(o5), "=&v"(o6), "=&v"(o7)
+        : "v"(w[k].x), "v"(w[k].y), "v"(w[k].z), "v"(w[k].w), "v"(s[k]));
+    // e0 + 8 is the next 16-byte chunk of the same block row
+    *reinterpret_cast<uint4*>(tb + off[k]) = make_uint4(o0, o1, o2, o3);
+    *reinterpret_cast<uint4*>(tb + (off[k] ^ 16)) = make_uint4(o4, o5, o6, o7);
+  }
+}
+
+// Item = (column block, row, 16-code quarter of the block): consecutive
+// lanes take the four quarters of consecutive rows of one block, so a
+// wave's bf16 stores stay inside one block (rows 128 B apart, chunks
+// swizzled) and its staging reads walk rows R bytes apart.  A thread's
+// items are loaded a few at a time before they are converted (two LDS
+// round trips per tile instead of one per item, within the registers the
+// kernel leaves free).
+template <class C>
+__device__ inline void convert_tile_e4(const unsigned char* __restrict__ st, unsigned char* __restrict__ tb, int tid) {
+  constexpr int ITEMS = C::E4_TILE / 16;
+  constexpr int PER = (ITEMS + C::NTHR - 1) / C::NTHR;
+  static_assert(ITEMS == (C::R / 64) * C::TILE * 4, "whole 64-column blocks");
+  constexpr int FIRST = (PER + 1) / 2;
+  convert_items_e4<C, FIRST>(st, tb, tid, 0);
+  convert_items_e4<C, PER - FIRST>(st, tb, tid, FIRST);
+}
+
 // DMA the trailing QL column blocks of q for this wave's 32 heads into LDS
 // (swizzled 128-byte rows, one per head); heads past H read as zeros.
 template <class C>
@@ -317,12 +440,17 @@ __device__ __forceinline__ void tile_step(const AttnArgs& a, unsigned char* __re
                                           int b, int k_issue, int tok0, int vis, int i, int wave, int lane,
                                           int dma_off, const int (&s_base)[4], const int (&tr_base)[2][2],
                                           const typename C::F::frag (&qf)[C::RKQ], float& m_run, float& l_run,
-                                          f32x16 (&O)[C::NTH][C::NCT]) {
+                                          f32x16 (&O)[C::NTH][C::NCT],
+                                          const unsigned char* __restrict__ conv_src = nullptr,
+                                          unsigned char* __restrict__ conv_dst = nullptr) {
   using T = typename C::T;
   using F = typename C::F;
   using frag = typename F::frag;
   const int hi = lane >> 5, l32 = lane & 31;
-  issue_tile<C>(a, dma_stage, b, k_issue, vis, wave, lane, dma_off, issue);
+  if constexpr (C::E4)
+    issue_tile_e4<C>(a, dma_stage, b, k_issue, vis, wave, lane, issue);
+  else
+    issue_tile<C>(a, dma_stage, b, k_issue, vis, wave, lane, dma_off, issue);
 
   // ---- S^T[32 tokens x 32 heads] = tile . q^T (one MFMA chain) --------
   auto a_frag = [&](int kb) -> frag {
@@ -413,6 +541,9 @@ __device__ __forceinline__ void tile_step(const AttnArgs& a, unsigned char* __re
   if (hi == 0) alpha_s[hl] = alpha;
   const bool any = __any(rebase);
   if (lane == 0) flag_s[wave] = any ? 1 : 0;
+  // E4M3: the codes of the next tile (DMA'd a step ago) are in for every
+  // wave behind this barrier; only this step's DMA may be in flight
+  if constexpr (C::E4) vm_wait<C::E4_LOADS>();
   lds_barrier();
 
   // ---- PV: O[all heads][this wave's columns] += P . tile ----------------
@@ -506,6 +637,9 @@ __device__ __forceinline__ void tile_step(const AttnArgs& a, unsigned char* __re
       }
     }
   }
+  // E4M3: convert the next tile into the other bf16 slot (its tile was
+  // finished a step ago); the next step's barrier publishes it
+  if constexpr (C::E4) convert_tile_e4<C>(conv_src, conv_dst, wave * 64 + lane);
 }
 
 template <class C>
@@ -575,7 +709,11 @@ __global__ __launch_bounds__(C::NTHR, 1) void attn_split_kernel(AttnArgs a) {
 
     // tile 0 first, then q, then the other prologue tiles: the wait before
     // tile 0 then also covers q, and later tiles stay in flight
-    issue_tile<C>(a, smem, b, k0, vis, wave, lane, dma_off, true);
+    unsigned char* e4_stage = smem + C::OFF_E4;  // E4M3 staging slots (E4 only)
+    if constexpr (C::E4)
+      issue_tile_e4<C>(a, e4_stage, b, k0, vis, wave, lane, true);
+    else
+      issue_tile<C>(a, smem, b, k0, vis, wave, lane, dma_off, true);
     asm volatile("" ::: "memory");  // keep the issue order: tile 0, q, tile 1
     // q^T fragments of this wave's 32 heads: the first RKQ k-steps in
     // registers, the trailing QL column blocks DMA'd into LDS (same
@@ -591,8 +729,12 @@ __global__ __launch_bounds__(C::NTHR, 1) void attn_split_kernel(AttnArgs a) {
       if constexpr (C::QL > 0) issue_q_tail<C>(a, smem, v, h_base, wave, lane);
     }
     asm volatile("" ::: "memory");
-    for (int s = 1; s < C::NSTAGE - 1; ++s)
-      issue_tile<C>(a, smem + s * C::TILE_BYTES, b, k0 + s, vis, wave, lane, dma_off, s < cnt);
+    if constexpr (C::E4) {
+      issue_tile_e4<C>(a, e4_stage + C::E4_STAGE, b, k0 + 1, vis, wave, lane, 1 < cnt);
+    } else {
+      for (int s = 1; s < C::NSTAGE - 1; ++s)
+        issue_tile<C>(a, smem + s * C::TILE_BYTES, b, k0 + s, vis, wave, lane, dma_off, s < cnt);
+    }
 
     float m_run = -1e30f, l_run = 0.f;
     f32x16 O[C::NTH][C::NCT];
@@ -601,14 +743,31 @@ __global__ __launch_bounds__(C::NTHR, 1) void attn_split_kernel(AttnArgs a) {
 #pragma unroll
       for (int ct = 0; ct < C::NCT; ++ct) O[ht][ct] = f32x16{};
 
-    auto step = [&](int i) {
-      // tiles i+1 .. i+NSTAGE-2 may stay in flight (zero-filled past the end)
-      vm_wait<(C::NSTAGE - 2) * n_loads>();
+    if constexpr (C::E4) {
+      // codes of tile 0 (and q) are in, tile 1 in flight: convert tile 0
+      vm_wait<C::E4_LOADS>();
       lds_barrier();
-      tile_step<C>(a, smem + ((i + C::NSTAGE - 1) % C::NSTAGE) * C::TILE_BYTES, smem + (i % C::NSTAGE) * C::TILE_BYTES,
-                   p_s, smem + C::OFF_Q + wave * 4096, alpha_s, flag_s, i + C::NSTAGE - 1 < cnt, b,
-                   k0 + i + C::NSTAGE - 1, (k0 + i) * C::TILE, vis, i, wave, lane, dma_off, s_base, tr_base, qf, m_run,
-                   l_run, O);
+      convert_tile_e4<C>(e4_stage, smem, tid);
+    }
+    auto step = [&](int i) {
+      if constexpr (C::E4) {
+        // tile i was converted into bf16 slot i % 2 at the end of the last
+        // step; the DMA of tile i + 2 goes into the staging slot of tile i
+        // (converted then too), and tile i + 1 is converted at the end
+        lds_barrier();
+        tile_step<C>(a, e4_stage + (i % 2) * C::E4_STAGE, smem + (i % 2) * C::TILE_BYTES, p_s,
+                     smem + C::OFF_Q + wave * 4096, alpha_s, flag_s, i + 2 < cnt, b, k0 + i + 2, (k0 + i) * C::TILE,
+                     vis, i, wave, lane, dma_off, s_base, tr_base, qf, m_run, l_run, O,
+                     e4_stage + ((i + 1) % 2) * C::E4_STAGE, smem + ((i + 1) % 2) * C::TILE_BYTES);
+      } else {
+        // tiles i+1 .. i+NSTAGE-2 may stay in flight (zero-filled past the end)
+        vm_wait<(C::NSTAGE - 2) * n_loads>();
+        lds_barrier();
+        tile_step<C>(a, smem + ((i + C::NSTAGE - 1) % C::NSTAGE) * C::TILE_BYTES, smem + (i % C::NSTAGE) * C::TILE_BYTES,
+                     p_s, smem + C::OFF_Q + wave * 4096, alpha_s, flag_s, i + C::NSTAGE - 1 < cnt, b,
+                     k0 + i + C::NSTAGE - 1, (k0 + i) * C::TILE, vis, i, wave, lane, dma_off, s_base, tr_base, qf,
+                     m_run, l_run, O);
+      }
     };
     // tile 0 is peeled: the compiler's wait for the q registers then lands
     // in front of its first use (leaving the DMA of tile 1 in flight)
@@ -931,10 +1090,12 @@ hipError_t launch_attention(const AttnArgs& a_in, bool bf16, hipStream_t s) {
   a.wrec = a.sched;
   a.srec = a.wrec + 8 * a.G;
   a.wfl = a.srec + 4 * a.U;
-  if (!bf16) return launch_attn_t<CfgF32>(a, s);
+  if (!bf16) return a.e4m3 ? hipErrorInvalidValue : launch_attn_t<CfgF32>(a, s);
   // one query token and one head group: every cache row is read by one
   // stream only, so its tiles are loaded non-temporally
-  return (a.n_q == 1 && a.n_hg == 1) ? launch_attn_t<CfgBf16Nt>(a, s) : launch_attn_t<CfgBf16>(a, s);
+  const bool nt = a.n_q == 1 && a.n_hg == 1;
+  if (a.e4m3) return nt ? launch_attn_t<CfgE4Nt>(a, s) : launch_attn_t<CfgE4>(a, s);
+  return nt ? launch_attn_t<CfgBf16Nt>(a, s) : launch_attn_t<CfgBf16>(a, s);
 }
 
 // ===========================================================================

@@ -85,6 +85,26 @@ struct AbsorbArgs {
 };
 hipError_t launch_absorb(const AbsorbArgs& a, bool bf16, hipStream_t s);
 
+// ------------------------------------------------------- cache store ----
+// Rows [M][R] fp32 into the cache slots of positions pos[b] + t (m = b*n_q+t),
+// RoPE'd first (columns d_latent.., append path) when `rope` is set: bf16
+// (RNE) or fp32 rows, or E4M3 codes with one power-of-two scale per row.
+struct StoreArgs {
+  const float* rows;
+  const int32_t* pos;
+  int M, n_q, R, d_latent, d_rope;
+  int rope;
+  float rope_base;
+  int format;             // 0: dtype rows, 1: E4M3 codes + scales
+  int bf16;               // dtype rows: bf16 (1) or fp32 (0)
+  void* pool;
+  float* scales;
+  const int32_t* page_table;
+  int paged, page_size, n_pages, max_pages, s_max;
+  int32_t* err;           // bit 1: position outside the cache, bit 2: page id outside the pool
+};
+hipError_t launch_cache_store(const StoreArgs& a, hipStream_t s);
+
 // ---------------------------------------------------------- attention ----
 struct AttnArgs {
   const void* q;               // [V][H][R]
@@ -106,6 +126,8 @@ struct AttnArgs {
   int32_t* err;
   float scale_log2;            // softmax scale * log2(e)
   int G;                       // attention work-groups
+  int e4m3;                    // cache rows are E4M3 codes with per-row scales
+  const float* scales;         // their scales, laid out like the rows
 };
 
 int attn_supported(bool bf16, int H, int d_latent, int d_rope);

@@ -31,6 +31,9 @@ class MLALayer:
     def append(self, x: torch.Tensor, pos: torch.Tensor, batch: int, n_q: int, cache: L.Cache, stream=None):
         L.mla_compress_append(self.dims, self.absorbed, x, pos, batch, n_q, cache, self.workspace, stream)
 
+    def store_rows(self, rows, pos, batch, n_q, cache: L.Cache, stream=None):
+        L.mla_cache_store_rows(self.dims, rows, pos, batch, n_q, cache, self.workspace, stream)
+
     def q_proj(self, x, kv_len, batch, n_q, q, stream=None):
         L.mla_q_proj(self.dims, self.absorbed, x, kv_len, batch, n_q, q, self.workspace, stream)
 

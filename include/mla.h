@@ -108,11 +108,30 @@ typedef struct mla_raw_weights {
   const void *W_DQ, *W_UQ, *W_QR, *W_DKV, *W_KR, *W_UK, *W_UV, *W_O;
 } mla_raw_weights;
 
-/* Latent cache.  Row width R = d_latent + d_rope elements of dtype.
+/* Row formats of the latent cache.  The pages leave the bytes per cache
+ * element open (page "Multi-Head Latent Attention: How DeepSeek Shrinks AI
+ * Memory", "What did DeepSeek's papers actually report?": about 6 bits per
+ * element in the served model; page "Multi-Head Latent Attention (MLA)",
+ * "Against the alternatives": quantisation as a separate axis).
+ *   MLA_ROWS_DTYPE: R elements of the layer dtype per row.
+ *   MLA_ROWS_E4M3:  (bf16 layers) R E4M3 codes per row (OCP e4m3fn: sign,
+ *     4 exponent bits with bias 7, 3 mantissa bits, largest finite 448),
+ *     and one fp32 scale per row; the row's values are code * scale.  The
+ *     library writes scale = 2^k with k the smallest integer such that the
+ *     row's largest |value| <= 448 * 2^k (k >= -126; 1 for a zero row), and
+ *     codes rounded to nearest, ties to even; every code * scale is then
+ *     exactly a bf16 value, which is what the attention computes with. */
+typedef enum mla_row_format { MLA_ROWS_DTYPE = 0, MLA_ROWS_E4M3 = 1 } mla_row_format;
+
+/* Latent cache.  Row width R = d_latent + d_rope elements.
  * Contiguous (page_table == NULL): pool is [batch, s_max, R].
  * Paged: pool is [n_pages, page_size, R]; token t of sequence b lives in
  * page page_table[b * max_pages_per_seq + t / page_size], slot
- * t % page_size.  page_size must be a positive multiple of 32. */
+ * t % page_size.  page_size must be a positive multiple of 32.
+ * row_format MLA_ROWS_E4M3: pool elements are one-byte codes and `scales`
+ * (4-byte aligned) holds one fp32 scale per row slot, laid out like the
+ * rows ([batch, s_max] or [n_pages, page_size]); otherwise scales is
+ * ignored.  The caller owns both buffers. */
 typedef struct mla_cache {
   void *pool;
   const int32_t *page_table;
@@ -120,6 +139,8 @@ typedef struct mla_cache {
   int32_t n_pages;
   int32_t max_pages_per_seq;
   int32_t s_max;
+  int32_t row_format; /* mla_row_format */
+  float *scales;
 } mla_cache;
 
 /* Human-readable name of a status code (static string). */
@@ -206,6 +227,20 @@ mla_status mla_read_device_error(void *workspace, int32_t *flags, void *stream);
 mla_status mla_compress_append(const mla_dims *dims, const void *absorbed, const void *x, const int32_t *pos,
                                int32_t batch, int32_t n_q, const mla_cache *cache, void *workspace,
                                size_t ws_bytes, void *stream);
+
+/* Writes given rows into the cache slots of positions pos[b] + t (token t
+ * of sequence b), as mla_compress_append writes the rows it computes:
+ * rounded to nearest even for a bf16 cache, copied for fp32, quantised as
+ * described at mla_row_format for MLA_ROWS_E4M3.  For loading or converting
+ * caches, and the reference point of the E4M3 quantiser.
+ *   rows [batch * n_q, R] fp32 device; pos [batch] int32 device
+ *   workspace: only its first 256 bytes, the device error word, are used
+ *   (any workspace of this library, or a zeroed 256-byte buffer)
+ * Positions outside the cache and page ids outside the pool set bits 1 and
+ * 2 of the device error word and leave the slot untouched. */
+mla_status mla_cache_store_rows(const mla_dims *dims, const float *rows, const int32_t *pos, int32_t batch,
+                                int32_t n_q, const mla_cache *cache, void *workspace, size_t ws_bytes,
+                                void *stream);
 
 /* Query projection with the merged query weight (page "Multi-Head Latent
  * Attention (MLA)", "Two merges", query side; "The RoPE problem"), or in the

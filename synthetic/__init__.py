@@ -8,10 +8,10 @@ other.
 from .configs import CONFIGS, MLAConfig, config
 from .inputs import (Case, bf16_bits, bf16_to_f32, round_bf16, make_case,
                      make_weights, make_lengths, make_page_table, make_rows,
-                     make_x, quiet_then_loud)
+                     make_e4m3_rows, make_x, quiet_then_loud)
 
 __all__ = [
     "CONFIGS", "MLAConfig", "config", "Case", "bf16_bits", "bf16_to_f32",
     "round_bf16", "make_case", "make_weights", "make_lengths",
-    "make_page_table", "make_rows", "make_x", "quiet_then_loud",
+    "make_page_table", "make_rows", "make_e4m3_rows", "make_x", "quiet_then_loud",
 ]

@@ -22,7 +22,7 @@ Drawing them directly keeps every decode input independent of the GPU path.
 from __future__ import annotations
 
 from dataclasses import dataclass, field
-from typing import Dict, List, Optional
+from typing import Dict, List, Optional, Tuple
 
 import numpy as np
 
@@ -159,6 +159,37 @@ def make_rows(cfg: MLAConfig, lengths: np.ndarray, rng: np.random.Generator,
     return out
 
 
+# Exponent-field weights of the synthetic E4M3 codes, fields 15 down to 8,
+# then the zero code: the binade masses of a normal draw with the std of
+# the bf16 rows of the V2 / V3 shapes (~1.43) at row scale 2^-6.  A row
+# drawn with scale 2^k shifts its fields down by k + 6, so every row's
+# values spread alike (as real rows do) whatever its scale.
+_E4_FIELD_P = np.array([0.01, 0.16, 0.32, 0.24, 0.13, 0.07, 0.04, 0.02, 0.01])
+_E4_K = np.array([-7, -6, -5])
+
+
+def make_e4m3_rows(cfg: MLAConfig, lengths: np.ndarray, rng: np.random.Generator
+                   ) -> List[Tuple[np.ndarray, np.ndarray]]:
+    """Synthetic E4M3 cache rows per sequence: (codes uint8 [S_b, R], row
+    scale exponents int32 [S_b]), drawn field by field — a uniform sign
+    bit, the exponent field from _E4_FIELD_P, a uniform mantissa (never the
+    NaN pattern), shifted against a scale exponent drawn from _E4_K per
+    row.  A row's values are code * 2^k."""
+    out = []
+    for s in lengths:
+        n = (int(s), cfg.row)
+        sign = rng.integers(0, 2, n)
+        pick = rng.choice(len(_E4_FIELD_P), size=n, p=_E4_FIELD_P)
+        k = rng.choice(_E4_K, size=int(s)).astype(np.int32)
+        field = np.minimum(15 - pick - (k[:, None] + 6), 15)
+        mant = rng.integers(0, 8, n)
+        mant = np.where((field == 15) & (mant == 7), 6, mant)
+        codes = (sign << 7) | (field << 3) | mant
+        codes = np.where(pick == len(_E4_FIELD_P) - 1, 0, codes).astype(np.uint8)
+        out.append((codes, k))
+    return out
+
+
 def make_x(cfg: MLAConfig, shape, rng: np.random.Generator) -> np.ndarray:
     return _finish(rng.standard_normal(shape, dtype=np.float32) * np.float32(_x_std(cfg)), cfg)
 
@@ -175,6 +206,8 @@ class Case:
     page_table: Optional[np.ndarray] = None
     n_pages: int = 0
     extra: dict = field(default_factory=dict)
+    # E4M3 rows (codes [S_b, R] uint8, scale exponents [S_b]), history="e4m3"
+    e4m3: Optional[List[Tuple[np.ndarray, np.ndarray]]] = None
 
     @property
     def kv_len(self) -> np.ndarray:
@@ -189,7 +222,10 @@ class Case:
 
 def make_case(cfg: MLAConfig, seed: int, history: str = "rows",
               spare_pages: int = 0, amplitude=None) -> Case:
-    """``amplitude``: optional per-row multipliers of the history rows
+    """``history``: "rows" (fp32 history rows), "x" (history activations)
+    or "e4m3" (E4M3 codes and scale exponents of every row a decode sees,
+    the new tokens' own rows included: make_e4m3_rows over cached + n_q).
+    ``amplitude``: optional per-row multipliers of the history rows
     (history="rows" only; see quiet_then_loud)."""
     rng = np.random.default_rng(seed)
     w = make_weights(cfg, rng)
@@ -197,13 +233,15 @@ def make_case(cfg: MLAConfig, seed: int, history: str = "rows",
     table, n_pages = (None, 0)
     if cfg.paged:
         table, n_pages = make_page_table(cached + cfg.n_q, cfg.page_size, rng, spare_pages)
-    rows = x_hist = None
+    rows = x_hist = e4m3 = None
     if history == "rows":
         rows = make_rows(cfg, cached, rng, amplitude)
     elif history == "x":
         x_hist = [make_x(cfg, (int(s), cfg.d_model), rng) for s in cached]
+    elif history == "e4m3":
+        e4m3 = make_e4m3_rows(cfg, cached + cfg.n_q, rng)
     else:
         raise ValueError(history)
     x_new = make_x(cfg, (cfg.batch, cfg.n_q, cfg.d_model), rng)
     return Case(cfg=cfg, seed=seed, weights=w, cached=cached, x_new=x_new,
-                rows=rows, x_hist=x_hist, page_table=table, n_pages=n_pages)
+                rows=rows, x_hist=x_hist, page_table=table, n_pages=n_pages, e4m3=e4m3)

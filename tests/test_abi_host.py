@@ -214,3 +214,33 @@ def test_smaller_prefill_calls_fit_the_sized_workspace():
         assert st == 0, (batch, n_q, st, mla._lib.load().mla_last_error())
     assert mla.mla_prefill_workspace_check(mla.make_dims(7168, 128, 512, 1536, 128, 64, 128, "bf16"), 2, 1024, 5120,
                                            ws_bytes) == -2  # needs the factored form
+
+
+def test_e4m3_cache_checks_before_launch():
+    """E4M3 cache rows: bf16 layers only, scales required and 4-byte
+    aligned, an unknown row format refused, no expanded prefill; all on the
+    host (placeholder device addresses are never dereferenced)."""
+    lib = _lib()
+    ws = ctypes.c_void_p(0x100000)
+
+    def attention(d, cache):
+        return lib.mla_attention(ctypes.byref(d), ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000), 16, 1,
+                                 ctypes.byref(cache), ctypes.c_void_p(0x3000), None, ws, 1 << 40, None)
+
+    E4 = mla.MLA_ROWS_E4M3
+    d = v2_dims()
+    assert attention(d, mla._lib.mla_cache(0x1000, None, 0, 0, 0, 4097, E4, None)) == -1        # no scales
+    assert attention(d, mla._lib.mla_cache(0x1000, None, 0, 0, 0, 4097, E4, 0x2002)) == -1      # misaligned
+    assert attention(d, mla._lib.mla_cache(0x1000, None, 0, 0, 0, 4097, 7, 0x2000)) == -1       # format 7
+    tiny = mla.make_dims(64, 4, 32, 48, 16, 8, 16, "f32")
+    assert attention(tiny, mla._lib.mla_cache(0x1000, None, 0, 0, 0, 64, E4, 0x2000)) == -2     # fp32 layer
+    f = mla.make_dims(7168, 128, 512, 1536, 128, 64, 128, "bf16", form="factored")
+    st = lib.mla_prefill_expanded(ctypes.byref(f), ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000),
+                                  ctypes.c_void_p(0x3000), 2, 8, ctypes.byref(mla._lib.mla_cache(
+                                      0x1000, None, 0, 0, 0, 64, E4, 0x2000)),
+                                  ctypes.c_void_p(0x4000), None, ws, 1 << 40, None)
+    assert st == -2                                                                              # no expanded prefill
+    st = lib.mla_cache_store_rows(ctypes.byref(d), ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000), 4, 1,
+                                  ctypes.byref(mla._lib.mla_cache(0x1000, None, 0, 0, 0, 64, E4, 0x2000)), ws, 128,
+                                  None)
+    assert st == -4                                                                              # < 256 workspace bytes
