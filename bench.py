@@ -34,7 +34,7 @@ BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 F32_PEAK_TFLOPS = 157.3      # MI355X dense fp32 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 MFMA_FILE = os.path.join(ROOT, "profiles", "mfma.txt")
-KERNEL_SOURCES = ("mla_gemm.hip", "mla_attn.hip", "mla_common.h")
+KERNEL_SOURCES = ("mla_gemm.hip", "mla_attn.hip", "mla_cache.hip", "mla_common.h")
 DEFAULT_CONFIG = 2
 ROOFLINE_CALL = "mla_attention"
 

@@ -18,7 +18,7 @@ profiles/mfma_<workload>.txt and, for bench.py's default workload,
 profiles/hbm_traffic.txt and profiles/mfma.txt (JSON read by bench.py: HBM
 bytes and MFMA counters per call, tagged with a hash of the kernel sources).
 
-    python bench_counters.py [--config N] [--out <dir for the raw profiler output>]
+    python bench_counters.py [--config N] [--cache dtype|e4m3] [--out <dir for the raw profiler output>]
 """
 from __future__ import annotations
 
@@ -94,7 +94,8 @@ def counters_per_dispatch(path):
 def steps(per_dispatch):
     """The bench steps in the dispatch list, each a list of (call, dispatch id).
 
-    A step is: the append GEMM, the two q-projection GEMMs, the attention
+    A step is: the append GEMM (followed by the quantising store kernel for
+    an E4M3 cache), the two q-projection GEMMs, the attention
     plan / split / merge kernels, then the output projection (its GEMM,
     preceded by the fp32 -> bf16 staging of o_lat when the large tiling
     takes it); a GEMM whose K range is split is followed by its epilogue
@@ -107,6 +108,9 @@ def steps(per_dispatch):
         groups, i = [], end - 1
         while len(groups) < count:
             g = [i]
+            if "cache_store" in names[i]:  # E4M3 append: its GEMM (+ epilogue), then the quantising store
+                i -= 1
+                g.insert(0, i)
             if "splitk_epilogue" in names[i]:
                 i -= 1
                 g.insert(0, i)
@@ -155,21 +159,23 @@ def trace_durations(path, skip=5):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--config", type=int, default=None, help="workload index (default: bench.py's)")
+    ap.add_argument("--cache", choices=("dtype", "e4m3"), default="dtype", help="bench.py --cache")
     ap.add_argument("--out", default=os.path.join(tempfile.gettempdir(), "mla_counters"))
     ap.add_argument("--profiles-dir", default=os.path.join(ROOT, "profiles"))
     ap.add_argument("--summarize-only", action="store_true",
                     help="rebuild the summaries from the profiler output already under --out")
     args = ap.parse_args()
     sys.path.insert(0, ROOT)
-    import bench
+    import bench as bench_mod
     if args.config is None:
-        args.config = bench.DEFAULT_CONFIG
+        args.config = bench_mod.DEFAULT_CONFIG
     # the profiler runs from /tmp: every path handed to it is absolute
     args.out = os.path.abspath(args.out)
     args.profiles_dir = os.path.abspath(args.profiles_dir)
     os.makedirs(args.out, exist_ok=True)
     py = sys.executable
-    bench = [py, os.path.join(ROOT, "bench.py"), "--config", str(args.config), "--no-cpu-baseline"]
+    bench = [py, os.path.join(ROOT, "bench.py"), "--config", str(args.config), "--no-cpu-baseline",
+             "--cache", args.cache]
     stats_cmd = ["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d",
                  os.path.join(args.out, "trace"), "-o", "run", "--"] + bench + ["--steps", "20", "--warmup", "5"]
     if not args.summarize_only:
@@ -246,7 +252,7 @@ def main():
         m["active"] += active * N_SIMD
     sys.path.insert(0, ROOT)
     from synthetic import config
-    workload = config(args.config).name
+    workload = config(args.config).name + ("_e4m3" if args.cache == "e4m3" else "")
 
     prof = args.profiles_dir
     os.makedirs(prof, exist_ok=True)
@@ -261,7 +267,7 @@ def main():
         f.write(f"# HBM traffic per dispatch, workload {workload}, last step of a 3-step bench run\n")
         for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
             f.write(f"# command: timeout -s KILL 120 rocprofv3 --pmc {ctr} --output-format csv -d <dir> -o run -- "
-                    f"python ./bench.py --config {args.config} --no-cpu-baseline --steps 3 --warmup 1\n")
+                    f"python ./bench.py --config {args.config} --no-cpu-baseline --cache {args.cache} --steps 3 --warmup 1\n")
             f.write(f"# calibration: timeout -s KILL 60 rocprofv3 --pmc {ctr} ... -- python ./bench.py "
                     f"--copy-calib-mb {COPY_MB} --steps 3 ; factor {factors[ctr]:.4f} bytes per counted byte\n")
         f.write(f"{'call':22s} {'kernel':70s} {'FETCH_KiB':>12s} {'WRITE_KiB':>12s} {'read_MB':>10s} {'write_MB':>10s}\n")
@@ -286,14 +292,14 @@ def main():
             f.write(f"# {c}: {m['flops'] / 1e9:.3f} GFLOP counted, {m['flops'] / (m['us'] * 1e-6) / 1e12:.1f} TFLOP/s "
                     f"({100 * m['flops'] / (m['us'] * 1e-6) / 2.5e15:.2f}% of peak), MFMA busy "
                     f"{100 * m['busy'] / max(m['active'], 1):.2f}% of SIMD cycles\n")
-    if args.config == bench.DEFAULT_CONFIG:
-        mout = {"workload": workload, "source_hash": bench.kernel_source_hash(), "flops_per_mop": flops_per_mop,
+    if args.config == bench_mod.DEFAULT_CONFIG and args.cache == "dtype":
+        mout = {"workload": workload, "source_hash": bench_mod.kernel_source_hash(), "flops_per_mop": flops_per_mop,
                 "calls": {c: {"gflop": round(m["flops"] / 1e9, 4),
                               "busy_pct": round(100 * m["busy"] / max(m["active"], 1), 2)} for c, m in mcalls.items()}}
         with open(os.path.join(prof, "mfma.txt"), "w") as f:
             json.dump(mout, f, indent=1)
             f.write("\n")
-        out = {"workload": workload, "source_hash": bench.kernel_source_hash(), "factors": factors,
+        out = {"workload": workload, "source_hash": bench_mod.kernel_source_hash(), "factors": factors,
                "calls": {c: round(v) for c, v in calls.items()}}
         with open(os.path.join(prof, "hbm_traffic.txt"), "w") as f:
             json.dump(out, f, indent=1)
