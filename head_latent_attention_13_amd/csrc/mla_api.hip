@@ -492,7 +492,9 @@ mla_status mla_workspace_size(const mla_dims* d, int32_t batch, int32_t n_q, siz
   mla_status st = check_common(d, nullptr, batch, n_q);
   if (st) return st;
   if (!bytes) return fail(MLA_ERR_INVALID_ARG, "bytes is NULL");
-  *bytes = ws_layout(d, batch, n_q).total;
+  const WsLayout W = ws_layout(d, batch, n_q);
+  if (!W.plans_ok) return fail(MLA_ERR_UNSUPPORTED, "no GEMM configuration fits the per-head factored products");
+  *bytes = W.total;
   return MLA_OK;
 }
 
