@@ -763,8 +763,9 @@ mla_status mla_prefill_expanded(const mla_dims* d, const void* absorbed, const v
   const AbsLayout L = abs_layout(d);
   const int H = d->n_heads, R = row_width(d), QE = d->d_nope + d->d_rope;
   float* part = reinterpret_cast<float*>(ws + P.part);
-  auto gemm = [&](const GemmPlan& g, bool a_f32, const void* A, int lda, const unsigned char* Wp, const EpiArgs& e) {
-    hipError_t err = launch_gemm(g, true, a_f32, A, lda, Wp, part, e, s);
+  auto gemm = [&](const GemmPlan& g, bool a_f32, const void* A, int lda, const unsigned char* Wp, const EpiArgs& e,
+                  const int32_t* row_len = nullptr) {
+    hipError_t err = launch_gemm(g, true, a_f32, A, lda, Wp, part, e, s, row_len, cache->s_max);
     return err == hipSuccess ? MLA_OK : hip_fail(err, "gemm launch");
   };
   // queries: c_Q, then [q_nope | RoPE(q_pe)] per head (192 wide)
@@ -778,11 +779,13 @@ mla_status mla_prefill_expanded(const mla_dims* d, const void* absorbed, const v
   if ((st = gemm(P.g_qn, false, cq, d->d_q_latent, ab + L.uq, e))) return st;
   e.qg_cols = d->d_rope; e.qg_stride = QE; e.q_off = d->d_nope; e.q_ld = H * QE; e.rope_from = 0;
   if ((st = gemm(P.g_qr, false, cq, d->d_q_latent, ab + L.qr, e))) return st;
-  // per-head keys and values of every cache slot: c W_UK[h], c W_UV[h]
+  // per-head keys and values of the cache slots below kv_len (the only ones
+  // the attention reads; blocks of slots past every sequence's length exit
+  // at once): c W_UK[h], c W_UV[h]
   void* ke = ws + P.ke;
   void* ve = ws + P.ve;
-  if ((st = gemm(P.g_k, false, cache->pool, R, ab + L.uk, base_epi(EPI_STORE_T, ke)))) return st;
-  if ((st = gemm(P.g_v, false, cache->pool, R, ab + L.uv, base_epi(EPI_STORE_T, ve)))) return st;
+  if ((st = gemm(P.g_k, false, cache->pool, R, ab + L.uk, base_epi(EPI_STORE_T, ke), kv_len))) return st;
+  if ((st = gemm(P.g_v, false, cache->pool, R, ab + L.uv, base_epi(EPI_STORE_T, ve), kv_len))) return st;
   // causal attention per head, then y = sum_h v[h] W_O[h]
   PrefillArgs a{};
   a.qe = qe; a.ke = ke; a.ve = ve; a.pool = cache->pool; a.kv_len = kv_len;

@@ -102,7 +102,22 @@ struct GemmArgs {
   int a_gtiles, a_gstride;  // A column groups (0: none)
   float* part;
   EpiArgs e;
+  const int32_t* row_len;   // needed rows per group of row_group rows (NULL: all)
+  int row_group;
 };
+
+// Whether any row of [m0, m1) is needed: row m of group b = m / row_group
+// is needed when m - b * row_group < row_len[b] (clamped to [0, row_group]).
+// Uniform across the block (scalar loads of the group lengths).
+__device__ inline bool rows_needed(const GemmArgs& g, int m0, int m1) {
+  if (!g.row_len) return true;
+  const int G = g.row_group;
+  for (int b = m0 / G; b * G < m1; ++b) {
+    const int lim = min(max(g.row_len[b], 0), G);
+    if (max(m0 - b * G, 0) < lim) return true;
+  }
+  return false;
+}
 
 // --------------------------------------------------------------------------
 // Streamed-weight GEMM with the epilogue fused when the K range is not split
@@ -126,6 +141,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   const int nt0 = blk.x * NGW * NT + (KSW == 1 ? wave * NT : 0);
   const int mt0 = blk.y * MT;
   const int ks = blk.z;
+  if (!rows_needed(g, mt0 * 16, min((mt0 + MT) * 16, M))) return;  // whole block
   int kb0 = ks * g.kb_per_split;
   int kb1 = min(kb0 + g.kb_per_split, g.kblocks);
   if (KSW > 1) {  // this wave's share of the slice
@@ -397,6 +413,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmArgs g) {
   const BlockXYZ blk = xcd_block();
   const int m0 = blk.x * C::BM, nt0 = blk.y * C::NTB;
   const int ks = blk.z;
+  if (!rows_needed(g, m0, min(m0 + C::BM, g.e.M))) return;  // whole block, before any DMA
   const int kb0 = ks * g.kb_per_split, kb1 = min(kb0 + g.kb_per_split, g.kblocks);
   const int nst = (kb1 - kb0 + C::SKB - 1) / C::SKB;  // stages in this slice
 
@@ -763,6 +780,7 @@ __global__ __launch_bounds__(256) void splitk_epilogue_kernel(GemmArgs g) {
   if (idx >= (long)g.e.M * pairs) return;
   const int m = (int)(idx / pairs);
   const int n = (int)(idx % pairs) * 2;
+  if (!rows_needed(g, m, m + 1)) return;  // its slices were not written
   // slices are loaded CH at a time (one memory round trip per chunk) and
   // summed in slice order
   constexpr int CH = 8;
@@ -1003,9 +1021,12 @@ hipError_t launch_f32_to_bf16(const float* x, void* y, size_t n, hipStream_t s) 
 }
 
 hipError_t launch_gemm(const GemmPlan& g, bool bf16, bool a_f32, const void* A, int lda, const void* Wp, float* part,
-                       const EpiArgs& e, hipStream_t s) {
+                       const EpiArgs& e, hipStream_t s, const int32_t* row_len, int row_group) {
   if (g.tiled < 0) return hipErrorInvalidConfiguration;
+  if (row_len && row_group <= 0) return hipErrorInvalidValue;
   GemmArgs a{};
+  a.row_len = row_len;
+  a.row_group = row_group;
   a.A = A;
   a.lda = lda;
   a.Wp = Wp;

@@ -72,8 +72,12 @@ GemmPlan plan_gemm(int M, int K, int N, bool bf16, bool a_f32, int n_cu, int a_g
 hipError_t launch_f32_to_bf16(const float* x, void* y, size_t n, hipStream_t s);
 
 // A is T (a_f32 == false) or fp32 (a_f32 == true); Wp is T.
+// row_len / row_group: rows m with m % row_group >= row_len[m / row_group]
+// (clamped to [0, row_group]) are not needed: blocks holding only such rows
+// return at once and leave their output rows unwritten (NULL: every row).
 hipError_t launch_gemm(const GemmPlan& g, bool bf16, bool a_f32, const void* A, int lda, const void* Wp, float* part,
-                       const EpiArgs& e, hipStream_t s);
+                       const EpiArgs& e, hipStream_t s,
+                       const int32_t* row_len = nullptr, int row_group = 0);
 
 // ------------------------------------------------------------- absorb ----
 struct AbsorbArgs {

@@ -121,3 +121,40 @@ def test_prefill_bad_length_is_flagged_and_contained():
     ref = OE.decode_step(case.weights, cfg.rope_base, cfg.softmax_scale, case.x_new[0], 20,
                          case.rows[0][:, :cfg.d_latent], case.rows[0][:, cfg.d_latent:])
     assert_close(yy[0], ref["y"], cfg, "y next to a bad sequence")
+
+
+def test_prefill_kv_gemms_stop_at_kv_len():
+    """A cache much longer than the sequences: the per-head key / value
+    up-projections cover only the slots below kv_len (row blocks past every
+    length exit at once), the result still matches the oracle, and the
+    slots past the lengths (NaN here) are never read."""
+    base = make_case(config(1), 1)
+    n_q, s_max = 64, 2048
+    cfg = config(1).with_(batch=2, cached=0, n_q=n_q, name="pkvlen")
+    rng = np.random.default_rng(4242)
+    cached = np.array([100, 236], dtype=np.int64)
+    case = Case(cfg=cfg, seed=25, weights=base.weights, cached=cached,
+                x_new=make_x(cfg, (2, n_q, cfg.d_model), rng), rows=make_rows(cfg, cached, rng))
+    layer = mla.MLALayer(dims_of(cfg, "factored"), upload_weights(case), max_batch=2, max_nq=n_q)
+    pool = torch.full((2, s_max, cfg.row), float("nan"), dtype=torch.bfloat16, device=DEV)
+    for b, r in enumerate(case.rows):
+        pool[b, :len(r)] = dev(r, cfg)
+    cache = mla.Cache(pool=pool, s_max=s_max)
+    need = mla.mla_prefill_workspace_size(layer.dims, 2, n_q, s_max)
+    ws = torch.full((need,), 0x5A, dtype=torch.uint8, device=DEV)
+    ws[:256] = 0  # the device error word
+    layer.pf_workspace = ws
+    note("prefill: kv_len far below s_max")
+    y, lse = prefill(layer, cfg, case, cache)
+    assert layer.prefill_error() == 0
+    y = y.view(2, n_q, cfg.d_model).cpu().numpy()
+    lse = lse.view(2, n_q, cfg.n_heads).cpu().numpy()
+    for b in range(2):
+        ref = OE.decode_step(case.weights, cfg.rope_base, cfg.softmax_scale, case.x_new[b], int(cached[b]),
+                             case.rows[b][:, :cfg.d_latent], case.rows[b][:, cfg.d_latent:])
+        assert_close(y[b], ref["y"], cfg, f"y[b={b}]")
+        assert_close(lse[b], ref["lse"], cfg, f"lse[b={b}]")
+    # keys and values of all 2 x 2048 slots would fill ~268 MB of the
+    # workspace; only the row blocks holding slots below kv_len are written
+    untouched = float((ws == 0x5A).float().mean())
+    assert untouched > 0.5, f"only {untouched:.2f} of the workspace left unwritten"
