@@ -146,6 +146,9 @@ struct WsLayout {
   GemmPlan g_qn, g_qr, g_qk, g_ov, g_oo;
   int G, V;
   bool plans_ok;
+  // factored form, up to 16 rows: c_Q unsplit, then one fused launch for
+  // q_nope, q_pe and q_lat (the per-head plans above are then unused)
+  bool q_fused;
   // o_lat goes through a bf16 copy (ob) before the merged output
   // projection when that runs LDS-tiled: every column block re-reads the
   // whole A operand (at 64 rows as many bytes as the weights), which the
@@ -176,7 +179,8 @@ WsLayout ws_layout(const mla_dims* d, int batch, int n_q, size_t cap = SIZE_MAX)
   const int M = batch * n_q, R = row_width(d), H = d->n_heads;
   const int ncu = device_cus();
   W.g_app = plan_gemm(M, d->d_model, R, bf, false, ncu, 0, 0, cap);
-  W.g_cq = plan_gemm(M, d->d_model, d->d_q_latent, bf, false, ncu, 0, 0, cap);
+  W.q_fused = factored(d) && q_fused_supported(bf, M, d->d_nope, d->d_rope, d->d_latent, d->d_q_latent);
+  W.g_cq = plan_gemm(M, d->d_model, d->d_q_latent, bf, false, ncu, 0, 0, W.q_fused ? 0 : cap);
   size_t part = std::max(W.g_app.part_bytes, W.g_cq.part_bytes);
   if (!factored(d)) {
     W.g_q = plan_gemm(M, d->d_q_latent, H * R, bf, false, ncu, 0, 0, cap);
@@ -327,6 +331,14 @@ mla_status q_proj_impl(const mla_dims* d, const WsLayout& W, const unsigned char
   }
   // factored: q_nope = c_Q W_UQ (all heads), rounded to dtype
   const int H = d->n_heads, R = row_width(d);
+  if (W.q_fused) {
+    QFusedArgs f{};
+    f.cq = cq; f.w_uq = abs + L.uq; f.w_qr = abs + L.qr; f.w_ukt = abs + L.ukt;
+    f.q = q; f.kv_len = kv_len;
+    f.M = batch * n_q; f.n_q = n_q; f.H = H; f.d_q_latent = d->d_q_latent; f.rope_base = d->rope_base;
+    hipError_t err = launch_q_fused(f, s);
+    return err == hipSuccess ? MLA_OK : hip_fail(err, "fused query projection launch");
+  }
   void* qn = ws + W.qn;
   st = run_gemm(W, G_Q, W.g_qn, bf, false, cq, d->d_q_latent, abs + L.uq, ws, base_epi(EPI_STORE_T, qn), s);
   if (st) return st;

@@ -1011,15 +1011,19 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   // Loads are issued CH pieces at a time (O values and LSEs together), so a
   // chunk costs one memory round trip.  Pass 1 forms the total LSE with a
   // running max; pass 2 weights the O values (the first chunk stays in
-  // registers from pass 1).
+  // registers from pass 1).  Only the chunk's real pieces are loaded (n is
+  // uniform over the block: scalar branches); the rest take LSE -inf.
   float4 x[CH];
   float lv[CH];
   auto load_chunk = [&](int base, bool with_o) {
 #pragma unroll
     for (int s = 0; s < CH; ++s) {
-      const int p = min(base + s, n - 1);  // clamped: lanes past n reload the last piece
-      lv[s] = pl[(size_t)p * HP];
-      if (with_o) x[s] = *reinterpret_cast<const float4*>(src + (size_t)p * HP * DL);
+      if (base + s < n) {
+        lv[s] = pl[(size_t)(base + s) * HP];
+        if (with_o) x[s] = *reinterpret_cast<const float4*>(src + (size_t)(base + s) * HP * DL);
+      } else {
+        lv[s] = -INFINITY;
+      }
     }
   };
   load_chunk(0, true);
@@ -1028,7 +1032,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
     if (base > 0) load_chunk(base, false);
     float cm = -INFINITY;
 #pragma unroll
-    for (int s = 0; s < CH; ++s) cm = fmaxf(cm, lv[s]);  // clamped entries repeat a real one
+    for (int s = 0; s < CH; ++s) cm = fmaxf(cm, lv[s]);  // at least one real piece
     const float nm = fmaxf(mx, cm);
     float cs = 0.f;
 #pragma unroll

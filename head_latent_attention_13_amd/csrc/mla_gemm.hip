@@ -1049,6 +1049,161 @@ hipError_t launch_gemm(const GemmPlan& g, bool bf16, bool a_f32, const void* A, 
 }
 
 // --------------------------------------------------------------------------
+// Factored query projection for up to 16 rows in one launch (after c_Q).
+// Block (head h, half j): phase A computes q_nope[h] = c_Q W_UQ[h] (all
+// 128 columns) together with half j of c_Q W_QR[h] (32 of 64 columns), the
+// four waves splitting K = d_q_latent and summing through LDS; q_nope is
+// rounded to bf16 into LDS (the rounding the unfused form applies when it
+// stores q_nope) and the q_pe half is rotated and stored.  Phase B computes
+// half j of q_lat[h] = q_nope[h] W_UK[h]^T (256 of 512 columns, K = 128),
+// each wave owning four 16-column tiles, staged through LDS into 16-byte
+// stores.  The two halves of a head are placed on one XCD (physical block
+// b runs on XCD b % 8), so the second read of W_UQ[h] is served by its L2.
+// --------------------------------------------------------------------------
+constexpr int kQfDn = 128, kQfDr = 64, kQfDl = 512;
+
+bool q_fused_supported(bool bf16, int M, int d_nope, int d_rope, int d_latent, int d_q_latent) {
+  return bf16 && M >= 1 && M <= 16 && d_nope == kQfDn && d_rope == kQfDr && d_latent == kQfDl &&
+         d_q_latent > 0 && d_q_latent % 32 == 0;
+}
+
+__global__ __launch_bounds__(256) void q_fused_kernel(QFusedArgs a) {
+  using F = Mfma<__bf16>;
+  using frag = F::frag;
+  constexpr int NTA = kQfDn / 16 + kQfDr / 32;  // phase A column tiles: 8 of q_nope, 2 of q_pe
+  constexpr int NTB = kQfDl / 2 / 16 / 4;       // phase B column tiles per wave
+  constexpr int KBB = kQfDn / 32;               // phase B k-blocks
+  constexpr int QS = kQfDn + 8;                 // q_nope row stride in LDS (bf16, padded)
+  constexpr int OS = kQfDl / 2 + 4;             // phase B staging row stride (fp32)
+  constexpr int R = kQfDl + kQfDr;              // q row width per head
+  __shared__ float red[4][16][NTA * 16];
+  __shared__ __attribute__((aligned(16))) __bf16 qn_s[16 * QS];
+  static_assert(16 * OS <= 4 * 16 * NTA * 16, "phase B staging fits the reduction buffer");
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int bid = blockIdx.x, xcd = bid & 7, slot = bid >> 3;
+  const int j = slot & 1, h = xcd + 8 * (slot >> 1);
+  if (h >= a.H) return;
+  const int M = a.M;
+  const int row = lane & 15, kq = 8 * (lane >> 4);
+  const bool rv = row < M;
+
+  // ---- phase A: K split over the waves ------------------------------------
+  const int KBA = a.d_q_latent / 32;
+  const int per = (KBA + 3) / 4;
+  const int kb0 = min(wave * per, KBA), kb1 = min(kb0 + per, KBA);
+  const __bf16* ap = reinterpret_cast<const __bf16*>(a.cq) + (size_t)(rv ? row : 0) * a.d_q_latent + kq;
+  const size_t ntu = (size_t)a.H * (kQfDn / 16), ntr = (size_t)a.H * (kQfDr / 16);
+  const __bf16* wu = reinterpret_cast<const __bf16*>(a.w_uq) + (size_t)h * (kQfDn / 16) * 512 + lane * 8;
+  const __bf16* wr = reinterpret_cast<const __bf16*>(a.w_qr) + ((size_t)h * (kQfDr / 16) + 2 * j) * 512 + lane * 8;
+  typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+  auto wload = [](const __bf16* p) {
+    return __builtin_bit_cast(frag, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
+  };
+  auto load = [&](frag (&bf)[NTA], frag& af, int kb) {
+#pragma unroll
+    for (int t = 0; t < kQfDn / 16; ++t) bf[t] = wload(wu + ((size_t)kb * ntu + t) * 512);
+#pragma unroll
+    for (int t = 0; t < kQfDr / 32; ++t) bf[kQfDn / 16 + t] = wload(wr + ((size_t)kb * ntr + t) * 512);
+    af = rv ? load_frag<__bf16>(ap + kb * 32) : F::zero();
+  };
+  f32x4 acc[NTA];
+#pragma unroll
+  for (int t = 0; t < NTA; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto mma = [&](const frag (&bf)[NTA], const frag& af) {
+#pragma unroll
+    for (int t = 0; t < NTA; ++t) acc[t] = F::mma(af, bf[t], acc[t]);
+  };
+  {
+    // two register buffers: the loads of k-block kb + 1 are in flight
+    // while the MFMAs of kb run
+    frag b0[NTA], b1[NTA], a0, a1;
+    int kb = kb0;
+    if (kb < kb1) load(b0, a0, kb);
+    while (kb < kb1) {
+      if (kb + 1 < kb1) load(b1, a1, kb + 1);
+      mma(b0, a0);
+      if (++kb >= kb1) break;
+      if (kb + 1 < kb1) load(b0, a0, kb + 1);
+      mma(b1, a1);
+      ++kb;
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NTA; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[wave][4 * (lane >> 4) + i][t * 16 + (lane & 15)] = acc[t][i];
+  // phase B weights do not depend on q_nope: in flight across the reduction
+  const size_t ntk = (size_t)a.H * (kQfDl / 16);
+  const __bf16* wk = reinterpret_cast<const __bf16*>(a.w_ukt) +
+                     ((size_t)h * (kQfDl / 16) + j * (kQfDl / 32) + wave * NTB) * 512 + lane * 8;
+  frag wb[KBB][NTB];
+#pragma unroll
+  for (int kb = 0; kb < KBB; ++kb)
+#pragma unroll
+    for (int t = 0; t < NTB; ++t) wb[kb][t] = wload(wk + ((size_t)kb * ntk + t) * 512);
+  __syncthreads();
+  // sums in wave order; q_nope -> bf16 LDS rows, q_pe pairs rotated and stored
+  for (int e = threadIdx.x; e < 16 * NTA * 8; e += 256) {
+    const int r = e / (NTA * 8), c = (e % (NTA * 8)) * 2;
+    float v0 = red[0][r][c], v1 = red[0][r][c + 1];
+#pragma unroll
+    for (int w2 = 1; w2 < 4; ++w2) {
+      v0 += red[w2][r][c];
+      v1 += red[w2][r][c + 1];
+    }
+    if (c < kQfDn) {
+      qn_s[r * QS + c] = (__bf16)v0;
+      qn_s[r * QS + c + 1] = (__bf16)v1;
+    } else if (r < M) {
+      const int f = 32 * j + (c - kQfDn);  // column within q_pe (even)
+      const int b = r / a.n_q, t = r - b * a.n_q;
+      float cs, sn;
+      rope_cos_sin(a.kv_len[b] - a.n_q + t, f >> 1, kQfDr, a.rope_base, &cs, &sn);
+      __bf16* y = reinterpret_cast<__bf16*>(a.q) + ((size_t)r * a.H + h) * R + kQfDl + f;
+      y[0] = (__bf16)(v0 * cs - v1 * sn);
+      y[1] = (__bf16)(v0 * sn + v1 * cs);
+    }
+  }
+  __syncthreads();
+
+  // ---- phase B: half j of q_nope[h] W_UK[h]^T -----------------------------
+  f32x4 accb[NTB];
+#pragma unroll
+  for (int t = 0; t < NTB; ++t) accb[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < KBB; ++kb) {
+    const frag af = *reinterpret_cast<const frag*>(qn_s + row * QS + kb * 32 + kq);
+#pragma unroll
+    for (int t = 0; t < NTB; ++t) accb[t] = F::mma(af, wb[kb][t], accb[t]);
+  }
+  float* ost = &red[0][0][0];  // [16][OS] fp32 (the reduction buffer is free)
+#pragma unroll
+  for (int t = 0; t < NTB; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ost[(4 * (lane >> 4) + i) * OS + (wave * NTB + t) * 16 + (lane & 15)] = accb[t][i];
+  __syncthreads();
+  for (int e = threadIdx.x; e < 16 * (kQfDl / 2 / 8); e += 256) {
+    const int r = e / (kQfDl / 2 / 8), ch = e % (kQfDl / 2 / 8);
+    if (r >= M) continue;
+    const float4 lo = *reinterpret_cast<const float4*>(ost + r * OS + 8 * ch);
+    const float4 hi = *reinterpret_cast<const float4*>(ost + r * OS + 8 * ch + 4);
+    bf16x8 v;
+    v[0] = (__bf16)lo.x; v[1] = (__bf16)lo.y; v[2] = (__bf16)lo.z; v[3] = (__bf16)lo.w;
+    v[4] = (__bf16)hi.x; v[5] = (__bf16)hi.y; v[6] = (__bf16)hi.z; v[7] = (__bf16)hi.w;
+    *reinterpret_cast<bf16x8*>(reinterpret_cast<__bf16*>(a.q) + ((size_t)r * a.H + h) * R + j * (kQfDl / 2) + 8 * ch) = v;
+  }
+}
+
+hipError_t launch_q_fused(const QFusedArgs& a, hipStream_t s) {
+  if (a.M < 1 || a.M > 16 || a.H < 1 || a.d_q_latent % 32 != 0) return hipErrorInvalidValue;
+  // two blocks per head, heads dealt 8 at a time over the XCDs
+  const int blocks = 16 * ((a.H + 7) / 8);
+  hipLaunchKernelGGL(q_fused_kernel, dim3(blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// --------------------------------------------------------------------------
 // Weight absorption (one-time).
 //
 // Packed outputs (K x N logical, see mla_common.h):

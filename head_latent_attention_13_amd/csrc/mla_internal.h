@@ -79,6 +79,25 @@ hipError_t launch_gemm(const GemmPlan& g, bool bf16, bool a_f32, const void* A, 
                        const EpiArgs& e, hipStream_t s,
                        const int32_t* row_len = nullptr, int row_group = 0);
 
+// Factored query projection after c_Q, in one launch, for up to 16 rows
+// (bf16; d_nope = 128, d_rope = 64, d_latent = 512, d_q_latent a multiple
+// of 32): per head h, q_nope = c_Q W_UQ[h] rounded to bf16, then
+// q[m][h] = [q_nope W_UK[h]^T | RoPE(c_Q W_QR[h])].  The weights are the
+// packed factors of the absorbed buffer (W_UQ: K = d_q_latent, N = H*128;
+// W_QR: N = H*64; W_UK^T: K = 128, N = H*512).
+struct QFusedArgs {
+  const void* cq;         // [M][d_q_latent] bf16
+  const void* w_uq;
+  const void* w_qr;
+  const void* w_ukt;
+  void* q;                // [M][H][576] bf16
+  const int32_t* kv_len;  // query t of sequence b sits at kv_len[b] - n_q + t
+  int M, n_q, H, d_q_latent;
+  float rope_base;
+};
+bool q_fused_supported(bool bf16, int M, int d_nope, int d_rope, int d_latent, int d_q_latent);
+hipError_t launch_q_fused(const QFusedArgs& a, hipStream_t s);
+
 // ------------------------------------------------------------- absorb ----
 struct AbsorbArgs {
   int d_model, H, d_latent, d_q_latent, d_nope, d_rope, d_v;

@@ -16,10 +16,11 @@ import pytest
 import torch
 
 import head_latent_attention_13_amd as mla
+from oracle import absorbed as OA
 from oracle import expanded as OE
 from synthetic import Case, config, make_case, make_rows, make_x
 
-from .gpu_common import (assert_close, contiguous_cache, dev, dims_of, i32, paged_cache, run_step, unpack,
+from .gpu_common import (DEV, assert_close, contiguous_cache, dev, dims_of, i32, paged_cache, run_step, unpack,
                          upload_weights)
 
 pytestmark = pytest.mark.gpu
@@ -186,3 +187,35 @@ def test_factored_edge_shapes(lengths, n_q):
         assert_close(o_lat[b], ref["o_lat"], cfg, f"o_lat[b={b}]")
         assert_close(y[b], ref["y"], cfg, f"y[b={b}]")
     assert layer.device_error() == 0
+
+
+@functools.lru_cache(maxsize=1)
+def _v2_merged_query_weight():
+    return OA.merged_weights(case_of(1).weights)[0]
+
+
+@pytest.mark.parametrize("batch,n_q", [(1, 1), (5, 1), (16, 1), (2, 8), (17, 1)])
+def test_factored_query_projection(batch, n_q):
+    """q = [c_Q W_UQ[h] W_UK[h]^T | RoPE(c_Q W_QR[h])] for every row and head
+    against the oracle's absorbed query (merged W_UQ[h] W_UK[h]^T in fp64):
+    up to 16 rows run as c_Q and one fused per-head launch, 17 rows through
+    the separate products; sequences sit at different positions, and 2 x 8
+    puts several queries of one sequence in a block."""
+    base = case_of(1)
+    cfg = base.cfg.with_(batch=batch, n_q=n_q, name=f"fq{batch}x{n_q}")
+    rng = np.random.default_rng(900 + 10 * batch + n_q)
+    x_new = make_x(cfg, (batch, n_q, cfg.d_model), rng)
+    cached = rng.integers(0, 3000, batch)
+    note(f"factored query projection {batch}x{n_q}")
+    layer = mla.MLALayer(dims_of(cfg, FORM), upload_weights(base), max_batch=batch, max_nq=n_q)
+    x = dev(x_new.reshape(batch * n_q, cfg.d_model), cfg)
+    q = torch.empty(batch * n_q, cfg.n_heads, cfg.row, dtype=torch.bfloat16, device=DEV)
+    layer.q_proj(x, i32(cached + n_q), batch, n_q, q)
+    torch.cuda.synchronize()
+    qg = q.float().cpu().numpy().reshape(batch, n_q, cfg.n_heads, cfg.row)
+    uqk = _v2_merged_query_weight()
+    for b in range(batch):
+        pos = np.arange(cached[b], cached[b] + n_q)
+        q_lat, q_pe = OA.query_latent(base.weights, uqk, x_new[b], pos, cfg.rope_base)
+        assert_close(qg[b, :, :, :cfg.d_latent], q_lat, cfg, f"q latent part b={b}")
+        assert_close(qg[b, :, :, cfg.d_latent:], q_pe, cfg, f"q rope part b={b}")
