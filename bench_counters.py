@@ -18,7 +18,8 @@ profiles/mfma_<workload>.txt and, for bench.py's default workload,
 profiles/hbm_traffic.txt and profiles/mfma.txt (JSON read by bench.py: HBM
 bytes and MFMA counters per call, tagged with a hash of the kernel sources).
 
-    python bench_counters.py [--config N] [--cache dtype|e4m3] [--out <dir for the raw profiler output>]
+    python bench_counters.py [--config N] [--cache dtype|e4m3] [--form merged|factored]
+                             [--out <dir for the raw profiler output>]
 """
 from __future__ import annotations
 
@@ -91,18 +92,28 @@ def counters_per_dispatch(path):
     return out
 
 
+# weight form of the profiled run (set by main): it fixes the launches per call
+FORM = "merged"
+
+
 def steps(per_dispatch):
     """The bench steps in the dispatch list, each a list of (call, dispatch id).
 
     A step is: the append GEMM (followed by the quantising store kernel for
-    an E4M3 cache), the two q-projection GEMMs, the attention
-    plan / split / merge kernels, then the output projection (its GEMM,
-    preceded by the fp32 -> bf16 staging of o_lat when the large tiling
-    takes it); a GEMM whose K range is split is followed by its epilogue
-    kernel.  Steps are anchored at their attention plan kernels."""
+    an E4M3 cache), the q-projection (merged: the c_Q and q GEMMs; factored:
+    the c_Q GEMM and the fused per-head kernel, or four GEMMs above 16
+    rows), the attention plan / split / merge kernels, then the output
+    projection (merged: its GEMM, preceded by the fp32 -> bf16 staging of
+    o_lat when the large tiling takes it; factored: two GEMMs); a GEMM whose
+    K range is split is followed by its epilogue kernel.  Steps are anchored
+    at their attention plan kernels."""
     ids = [d for d in sorted(per_dispatch) if mla_kernel(per_dispatch[d][0])]
     names = [per_dispatch[d][0] for d in ids]
     plans = [i for i, n in enumerate(names) if "attn_plan" in n]
+    q_groups, out_groups = 2, 1
+    if FORM == "factored":
+        out_groups = 2
+        q_groups = 2 if any("q_fused" in n for n in names) else 4
 
     def gemm_groups_before(end, count):
         groups, i = [], end - 1
@@ -122,17 +133,20 @@ def steps(per_dispatch):
     for plan in plans:
         if plan < 3:
             continue
-        pre = gemm_groups_before(plan, 3)
+        pre = gemm_groups_before(plan, 1 + q_groups)
         calls = [("mla_compress_append", i) for i in pre[0]] + [("mla_q_proj", i) for g in pre[1:] for i in g]
         calls += [("mla_attention", plan), ("mla_attention", plan + 1), ("mla_attention", plan + 2)]
         i = plan + 3
         if i < len(names) and "f32_to_bf16" in names[i]:
             calls.append(("mla_out_proj", i))
             i += 1
-        if i < len(names):
-            calls.append(("mla_out_proj", i))
-            if i + 1 < len(names) and "splitk_epilogue" in names[i + 1]:
-                calls.append(("mla_out_proj", i + 1))
+        for _ in range(out_groups):
+            if i < len(names):
+                calls.append(("mla_out_proj", i))
+                i += 1
+            if i < len(names) and "splitk_epilogue" in names[i]:
+                calls.append(("mla_out_proj", i))
+                i += 1
         out.append([(c, ids[k]) for c, k in calls])
     return out
 
@@ -160,11 +174,14 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--config", type=int, default=None, help="workload index (default: bench.py's)")
     ap.add_argument("--cache", choices=("dtype", "e4m3"), default="dtype", help="bench.py --cache")
+    ap.add_argument("--form", choices=("merged", "factored"), default="merged", help="bench.py --form")
     ap.add_argument("--out", default=os.path.join(tempfile.gettempdir(), "mla_counters"))
     ap.add_argument("--profiles-dir", default=os.path.join(ROOT, "profiles"))
     ap.add_argument("--summarize-only", action="store_true",
                     help="rebuild the summaries from the profiler output already under --out")
     args = ap.parse_args()
+    global FORM
+    FORM = args.form
     sys.path.insert(0, ROOT)
     import bench as bench_mod
     if args.config is None:
@@ -175,7 +192,7 @@ def main():
     os.makedirs(args.out, exist_ok=True)
     py = sys.executable
     bench = [py, os.path.join(ROOT, "bench.py"), "--config", str(args.config), "--no-cpu-baseline",
-             "--cache", args.cache]
+             "--cache", args.cache] + (["--form", args.form] if args.form != "merged" else [])
     stats_cmd = ["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d",
                  os.path.join(args.out, "trace"), "-o", "run", "--"] + bench + ["--steps", "20", "--warmup", "5"]
     if not args.summarize_only:
@@ -252,7 +269,9 @@ def main():
         m["active"] += active * N_SIMD
     sys.path.insert(0, ROOT)
     from synthetic import config
-    workload = config(args.config).name + ("_e4m3" if args.cache == "e4m3" else "")
+    workload = (config(args.config).name + ("_e4m3" if args.cache == "e4m3" else "") +
+                ("_factored" if args.form == "factored" else ""))
+    form_arg = f" --form {args.form}" if args.form != "merged" else ""
 
     prof = args.profiles_dir
     os.makedirs(prof, exist_ok=True)
@@ -267,7 +286,8 @@ def main():
         f.write(f"# HBM traffic per dispatch, workload {workload}, last step of a 3-step bench run\n")
         for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
             f.write(f"# command: timeout -s KILL 120 rocprofv3 --pmc {ctr} --output-format csv -d <dir> -o run -- "
-                    f"python ./bench.py --config {args.config} --no-cpu-baseline --cache {args.cache} --steps 3 --warmup 1\n")
+                    f"python ./bench.py --config {args.config} --no-cpu-baseline --cache {args.cache}{form_arg} "
+                    f"--steps 3 --warmup 1\n")
             f.write(f"# calibration: timeout -s KILL 60 rocprofv3 --pmc {ctr} ... -- python ./bench.py "
                     f"--copy-calib-mb {COPY_MB} --steps 3 ; factor {factors[ctr]:.4f} bytes per counted byte\n")
         f.write(f"{'call':22s} {'kernel':70s} {'FETCH_KiB':>12s} {'WRITE_KiB':>12s} {'read_MB':>10s} {'write_MB':>10s}\n")
@@ -292,7 +312,7 @@ def main():
             f.write(f"# {c}: {m['flops'] / 1e9:.3f} GFLOP counted, {m['flops'] / (m['us'] * 1e-6) / 1e12:.1f} TFLOP/s "
                     f"({100 * m['flops'] / (m['us'] * 1e-6) / 2.5e15:.2f}% of peak), MFMA busy "
                     f"{100 * m['busy'] / max(m['active'], 1):.2f}% of SIMD cycles\n")
-    if args.config == bench_mod.DEFAULT_CONFIG and args.cache == "dtype":
+    if args.config == bench_mod.DEFAULT_CONFIG and args.cache == "dtype" and args.form == "merged":
         mout = {"workload": workload, "source_hash": bench_mod.kernel_source_hash(), "flops_per_mop": flops_per_mop,
                 "calls": {c: {"gflop": round(m["flops"] / 1e9, 4),
                               "busy_pct": round(100 * m["busy"] / max(m["active"], 1), 2)} for c, m in mcalls.items()}}
