@@ -1320,6 +1320,113 @@ __global__ __launch_bounds__(256) void absorb_product_kernel(ProdArgs p) {
   }
 }
 
+// Per-head products for bf16 weights with K = 128 and 64-divisible sides, one
+// 64 x 64 output tile of one head per work-group: A (rows x 128, k
+// contiguous) and B (read as columns x 128, k contiguous in LDS: W_UK[h]
+// is stored that way, W_O[h] is stored k-major and transposed on its way
+// into LDS) are staged with 16-byte loads; each wave takes 16 rows and
+// four 16-column tiles through the same 16x16x32 MFMAs, in the same k
+// order, as absorb_product_kernel, so the products are bit-identical; the
+// tile goes back through LDS column-major and leaves as whole 1 KB packed
+// fragments (16 bytes per lane).
+constexpr int kAbK = 128, kAbT = 64, kAbS = kAbK + 8;  // LDS row stride (bf16), padded
+
+// Shapes, strides (in elements) and pointers the tiled kernel's 16-byte
+// accesses need; anything else takes absorb_product_kernel.
+static bool absorb_tiled_ok(const ProdArgs& p, bool b_kmajor) {
+  auto a16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+  const bool b_ok = b_kmajor ? (p.b_ds % 8 == 0 && p.b_cs == 1) : (p.b_cs % 8 == 0 && p.b_ds == 1);
+  return p.kd == kAbK && p.rows % kAbT == 0 && p.cols % kAbT == 0 && p.k_hs % 32 == 0 && p.n_hs % 16 == 0 &&
+         p.a_ds == 1 && p.a_rs % 8 == 0 && p.a_hs % 8 == 0 && p.b_hs % 8 == 0 && b_ok && a16(p.Ab) && a16(p.Bb) &&
+         a16(p.out);
+}
+
+template <bool B_KMAJOR>
+__global__ __launch_bounds__(256) void absorb_tile_kernel(ProdArgs p) {
+  using F = Mfma<__bf16>;
+  __shared__ __attribute__((aligned(16))) __bf16 as[kAbT * kAbS];
+  __shared__ __attribute__((aligned(16))) __bf16 bs[kAbT * kAbS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ct_n = p.cols / kAbT, rt_n = p.rows / kAbT;
+  const int ct = blockIdx.x % ct_n, rt = (blockIdx.x / ct_n) % rt_n, h = blockIdx.x / (ct_n * rt_n);
+  const int r0 = rt * kAbT, c0 = ct * kAbT;
+  const __bf16* Ab = reinterpret_cast<const __bf16*>(p.Ab) + (long)h * p.a_hs;
+  const __bf16* Bb = reinterpret_cast<const __bf16*>(p.Bb) + (long)h * p.b_hs;
+  // A rows r0.. (k contiguous): 64 rows x 16 chunks of 8
+  for (int q = tid; q < kAbT * (kAbK / 8); q += 256) {
+    const int r = q / (kAbK / 8), ch = q % (kAbK / 8);
+    *reinterpret_cast<bf16x8*>(as + r * kAbS + 8 * ch) =
+        *reinterpret_cast<const bf16x8*>(Ab + (long)(r0 + r) * p.a_rs + 8 * ch);
+  }
+  if constexpr (!B_KMAJOR) {
+    // B column c at Bb[c * b_cs + d] (k contiguous)
+    for (int q = tid; q < kAbT * (kAbK / 8); q += 256) {
+      const int c = q / (kAbK / 8), ch = q % (kAbK / 8);
+      *reinterpret_cast<bf16x8*>(bs + c * kAbS + 8 * ch) =
+          *reinterpret_cast<const bf16x8*>(Bb + (long)(c0 + c) * p.b_cs + 8 * ch);
+    }
+  } else {
+    // B row d at Bb[d * b_ds + c] (columns contiguous): transposed into LDS
+    for (int q = tid; q < kAbK * (kAbT / 8); q += 256) {
+      const int d = q / (kAbT / 8), cc = q % (kAbT / 8);
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(Bb + (long)d * p.b_ds + c0 + 8 * cc);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) bs[(8 * cc + j) * kAbS + d] = v[j];
+    }
+  }
+  __syncthreads();
+  f32x4 acc[kAbT / 16];
+#pragma unroll
+  for (int t = 0; t < kAbT / 16; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int rl = 16 * wave + (lane & 15), kq = 8 * (lane >> 4);
+#pragma unroll
+  for (int ks = 0; ks < kAbK / 32; ++ks) {
+    const bf16x8 af = *reinterpret_cast<const bf16x8*>(as + rl * kAbS + 32 * ks + kq);
+#pragma unroll
+    for (int t = 0; t < kAbT / 16; ++t) {
+      const bf16x8 bf = *reinterpret_cast<const bf16x8*>(bs + (16 * t + (lane & 15)) * kAbS + 32 * ks + kq);
+      acc[t] = F::mma(af, bf, acc[t]);
+    }
+  }
+  __syncthreads();
+  // column-major tile in the A buffer: element (r, c) at as[c * kAbS + r]
+#pragma unroll
+  for (int t = 0; t < kAbT / 16; ++t) {
+    __bf16 v4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v4[i] = (__bf16)acc[t][i];
+    *reinterpret_cast<uint2*>(as + (16 * t + (lane & 15)) * kAbS + 16 * wave + 4 * (lane >> 4)) =
+        *reinterpret_cast<const uint2*>(v4);
+  }
+  __syncthreads();
+  // packed fragments (k-block kb, column tile nt): lane l holds rows
+  // 32 kb + 8 (l / 16) .. + 7 of column 16 nt + l % 16
+  __bf16* out = reinterpret_cast<__bf16*>(p.out);
+  const long kb0 = ((long)h * p.k_hs + r0) / 32, nt0 = ((long)h * p.n_hs + c0) / 16;
+  for (int f = wave; f < (kAbT / 32) * (kAbT / 16); f += 4) {
+    const int kb = f / (kAbT / 16), nt = f % (kAbT / 16);
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(as + (16 * nt + (lane & 15)) * kAbS + 32 * kb + kq);
+    *reinterpret_cast<bf16x8*>(out + (((kb0 + kb) * (long)(p.Np / 16) + nt0 + nt) * 64 + lane) * 8) = v;
+  }
+}
+
+template <typename T>
+static hipError_t launch_product(const ProdArgs& p, bool b_kmajor, hipStream_t s) {
+  if constexpr (sizeof(T) == 2) {
+    if (absorb_tiled_ok(p, b_kmajor)) {
+      const unsigned blocks = (unsigned)((long)p.H * (p.rows / kAbT) * (p.cols / kAbT));
+      if (b_kmajor)
+        hipLaunchKernelGGL(absorb_tile_kernel<true>, dim3(blocks), dim3(256), 0, s, p);
+      else
+        hipLaunchKernelGGL(absorb_tile_kernel<false>, dim3(blocks), dim3(256), 0, s, p);
+      return hipGetLastError();
+    }
+  }
+  const long tiles = (long)p.H * ceil_div(p.rows, 16) * ceil_div(p.cols, 16);
+  hipLaunchKernelGGL(absorb_product_kernel<T>, dim3((unsigned)((tiles + 3) / 4)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
 template <typename T>
 static hipError_t pack_one(const AbsorbArgs& a, int mode, int K, int N, void* out, const void* plain, long ld,
                            hipStream_t s) {
@@ -1377,9 +1484,7 @@ static hipError_t absorb_t(const AbsorbArgs& a, hipStream_t s) {
     p.Bb = a.W_UK; p.b_hs = a.d_nope; p.b_ds = 1; p.b_cs = (long)a.H * a.d_nope;
     p.H = a.H; p.rows = a.d_q_latent; p.cols = a.d_latent; p.kd = a.d_nope;
     p.k_hs = 0; p.n_hs = R; p.Np = ceil_div(a.H * R, 16) * 16; p.out = a.P_QC;
-    const long tiles = (long)a.H * ceil_div(p.rows, 16) * ceil_div(p.cols, 16);
-    hipLaunchKernelGGL(absorb_product_kernel<T>, dim3((unsigned)((tiles + 3) / 4)), dim3(256), 0, s, p);
-    hipError_t err = hipGetLastError();
+    hipError_t err = launch_product<T>(p, false, s);
     if (err != hipSuccess) return err;
   }
   // W_UVO[h] = W_UV[h] W_O[h] : rows d_L, cols d_model, reduce over d_v
@@ -1389,9 +1494,7 @@ static hipError_t absorb_t(const AbsorbArgs& a, hipStream_t s) {
     p.Bb = a.W_O; p.b_hs = (long)a.d_v * a.d_model; p.b_ds = a.d_model; p.b_cs = 1;
     p.H = a.H; p.rows = a.d_latent; p.cols = a.d_model; p.kd = a.d_v;
     p.k_hs = a.d_latent; p.n_hs = 0; p.Np = ceil_div(a.d_model, 16) * 16; p.out = a.P_O;
-    const long tiles = (long)a.H * ceil_div(p.rows, 16) * ceil_div(p.cols, 16);
-    hipLaunchKernelGGL(absorb_product_kernel<T>, dim3((unsigned)((tiles + 3) / 4)), dim3(256), 0, s, p);
-    hipError_t err = hipGetLastError();
+    hipError_t err = launch_product<T>(p, true, s);
     if (err != hipSuccess) return err;
   }
   return hipSuccess;

@@ -99,6 +99,50 @@ def test_tiny_f32_absorbed_weights():
     assert np.array_equal(kv[:, :L], case.weights["W_DKV"]) and np.array_equal(kv[:, L:], case.weights["W_KR"])
 
 
+def test_v2_absorbed_weights_bf16():
+    """The merged bf16 products of the V2 layer, W_UQ[h] W_UK[h]^T and
+    W_UV[h] W_O[h] (page "Multi-Head Latent Attention (MLA)", "Two merges"),
+    for sampled heads: every element within one bf16 step of the fp32
+    product of the bf16 factors (the products run in fp32 and are rounded
+    once; only the order of the fp32 sums may differ), the W_QR columns and
+    the down-projections copied exactly."""
+    case = case_of(1)
+    cfg = case.cfg
+    note("v2 absorbed weights: pack + products")
+    layer = mla.MLALayer(dims_of(cfg), upload_weights(case), max_batch=1)
+    torch.cuda.synchronize()
+    offs, sizes, _ = mla.mla_absorbed_layout(layer.dims)
+    H, R, L, LQ, D = cfg.n_heads, cfg.row, cfg.d_latent, cfg.d_q_latent, cfg.d_model
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16).float().numpy()
+
+    def packed(i, lo=0, n=None):
+        n = sizes[i] // 2 if n is None else n
+        t = layer.absorbed[offs[i] + 2 * lo:offs[i] + 2 * (lo + n)].view(torch.bfloat16)
+        return t.float().cpu().numpy()
+
+    def within_one_step(got, a, b, what):
+        # one bf16 step of the reference, plus what a different order of the
+        # fp32 sums can move it: 2^-21 of the sum of the terms' magnitudes
+        ref = bf(a @ b)
+        step = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 7)
+        bad = np.abs(got - ref) > step + 2.0 ** -21 * (np.abs(a) @ np.abs(b))
+        assert not bad.any(), f"{what}: {int(bad.sum())} elements off by more than one bf16 step"
+
+    W = {k: bf(v) for k, v in case.weights.items()}
+    qc = unpack(packed(2), LQ, H * R, True).reshape(LQ, H, R)
+    w_o = W["W_O"].reshape(H, cfg.d_v, D)
+    frag = 320 * 512  # elements of one k-block of the packed W_UVO (d_model / 16 fragments)
+    for h in (0, 37, 127):
+        within_one_step(qc[:, h, :L], W["W_UQ"][:, h, :], W["W_UK"][:, h, :].T, f"W_UQ W_UK^T head {h}")
+        assert np.array_equal(qc[:, h, L:], W["W_QR"][:, h, :]), f"W_QR head {h}"
+        o_h = unpack(packed(3, h * (L // 32) * frag, (L // 32) * frag), L, D, True)
+        within_one_step(o_h, W["W_UV"][:, h, :], w_o[h], f"W_UV W_O head {h}")
+    kv = unpack(packed(0), cfg.d_model, R, True)
+    assert np.array_equal(kv[:, :L], W["W_DKV"]) and np.array_equal(kv[:, L:], W["W_KR"])
+
+
 # ----------------------------------------------------- V2 end-to-end slice ----
 def test_v2_end_to_end_from_activations():
     """Two sequences of the V2 shape, 4096 history tokens each, appended by
