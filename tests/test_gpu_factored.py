@@ -219,3 +219,24 @@ def test_factored_query_projection(batch, n_q):
         q_lat, q_pe = OA.query_latent(base.weights, uqk, x_new[b], pos, cfg.rope_base)
         assert_close(qg[b, :, :, :cfg.d_latent], q_lat, cfg, f"q latent part b={b}")
         assert_close(qg[b, :, :, cfg.d_latent:], q_pe, cfg, f"q rope part b={b}")
+
+
+@pytest.mark.parametrize("form", ["factored", "merged"])
+def test_decode_twelve_heads(form):
+    """Twelve heads at the V2 widths: in the factored form the fused query
+    kernel covers heads 0..11 of its 16 (the rest exit), in the merged form
+    the tiled absorption builds 12 heads' products; the attention runs one
+    partial head group.  o_lat, lse and y of every sequence against the
+    oracle."""
+    cfg = config(1).with_(n_heads=12, batch=3, cached=(700, 1300), name="heads12")
+    case = make_case(cfg, seed=41)
+    note(f"{form}, 12 heads: pack + cache")
+    layer = mla.MLALayer(dims_of(cfg, form), upload_weights(case), max_batch=cfg.batch)
+    cache, _ = contiguous_cache(cfg, case.rows, int(case.cached.max()) + 1)
+    o_lat, lse, y = run_step(layer, cfg, case, cache)
+    for b in range(cfg.batch):
+        ref = oracle_seq(case, b)
+        assert_close(o_lat.cpu().numpy()[b], ref["o_lat"][0], cfg, f"o_lat[b={b}]")
+        assert_close(lse.cpu().numpy()[b], ref["lse"][0], cfg, f"lse[b={b}]")
+        assert_close(y.cpu().numpy()[b], ref["y"][0], cfg, f"y[b={b}]")
+    assert layer.device_error() == 0
