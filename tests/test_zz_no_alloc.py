@@ -123,6 +123,27 @@ def test_capped_split_many_sequences():
     assert torch.equal(o, o_ref) and torch.equal(lse, l_ref)
 
 
+def test_e4m3_cache_matches_the_workspace_entry_point():
+    """An E4M3 latent cache (codes and per-row scales written by
+    mla_cache_store_rows): the no-allocation entry point converts the same
+    tiles as mla_attention and matches it bit for bit at the same split."""
+    dims = dims_of(CFG)
+    kv = [300, 1537, 64, 4097]
+    B, S = len(kv), max(kv)
+    rows = torch.randn(B * S, R, generator=_gen(71), device=DEV) * 0.5
+    pool = torch.zeros(B, S, R, dtype=torch.uint8, device=DEV)
+    scales = torch.zeros(B, S, dtype=torch.float32, device=DEV)
+    cache = mla.Cache(pool=pool, s_max=S, scales=scales)
+    ws = torch.zeros(256, dtype=torch.uint8, device=DEV)
+    note("E4M3 cache: 4 sequences, 64..4097 rows")
+    mla.mla_cache_store_rows(dims, rows, torch.zeros(B, dtype=torch.int32, device=DEV), B, S, cache, ws)
+    torch.cuda.synchronize()
+    assert mla.mla_read_device_error(ws) == 0
+    o, lse, o_ref, l_ref = both(kv, 1, cache, 72)
+    assert torch.equal(o, o_ref) and torch.equal(lse, l_ref), "same split: bit-identical"
+    assert torch.isfinite(o).all()
+
+
 def test_device_error_word_and_limits():
     dims = dims_of(CFG)
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
