@@ -263,6 +263,34 @@ __device__ inline void dma_column_blocks(__amdgpu_buffer_rsrc_t rsrc, unsigned c
 // outside the pool (which also raises error bit 2), and a tile past the end
 // of the segment (`live` false) all read as zeros.  Every call issues the same NINST / NW loads per wave,
 // so the pipeline can wait on a constant count.
+// Buffer record of tile k (page lookup, visible bytes), as issue_tile uses.
+template <class C>
+__device__ inline __amdgpu_buffer_rsrc_t tile_rsrc(const AttnArgs& a, int b, int k, int vis, int lane, bool live) {
+  const int t0 = k * C::TILE;
+  const unsigned char* gbase = reinterpret_cast<const unsigned char*>(a.pool);
+  bool ok = live;
+  if (live) {
+    if (a.paged) {
+      const int pg = MLA_CONST_PTR(a.page_table)[(size_t)b * a.max_pages + t0 / a.page_size];
+      ok = (pg >= 0) && (pg < a.n_pages);
+      if (!ok && lane == 0) atomicOr(a.err, 2);  // flagged, then read as zeros
+      gbase += ((size_t)(ok ? pg : 0) * a.page_size + (t0 % a.page_size)) * (size_t)C::ROW_BYTES;
+    } else {
+      gbase += ((size_t)b * a.s_max + t0) * (size_t)C::ROW_BYTES;
+    }
+  }
+  const int nbytes = ok ? min(max(vis - t0, 0), C::TILE) * C::ROW_BYTES : 0;
+  return make_rsrc(gbase, nbytes);
+}
+
+// Column block KK of a FAST tile (see issue_tile), for loads issued one at a
+// time between other work.
+template <class C, int KK>
+__device__ inline void dma_block(__amdgpu_buffer_rsrc_t rsrc, unsigned char* stage, int wave, int dma_off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, MLA_LDS_PTR(stage + (wave + 4 * KK) * 1024), 16, dma_off, KK * 128,
+                                           0, C::CNT ? 2 : 0);
+}
+
 template <class C>
 __device__ inline void issue_tile(const AttnArgs& a, unsigned char* stage, int b, int k, int vis, int wave,
                                   int lane, int dma_off, bool live) {
@@ -447,8 +475,16 @@ __device__ __forceinline__ void tile_step(const AttnArgs& a, unsigned char* __re
   using F = typename C::F;
   using frag = typename F::frag;
   const int hi = lane >> 5, l32 = lane & 31;
+  // DMA of the tile NSTAGE-1 ahead.  FAST bf16 tiles: the buffer record
+  // (and the page lookup) now, the nine loads spread over the score MFMAs,
+  // one every four k-steps: issued back to back, the four waves' 36 loads
+  // held each wave for ~600 clocks while the address unit drained them.
+  constexpr bool SPREAD = C::FAST && !C::E4;
+  __amdgpu_buffer_rsrc_t dma_rsrc;
   if constexpr (C::E4)
     issue_tile_e4<C>(a, dma_stage, b, k_issue, vis, wave, lane, issue);
+  else if constexpr (SPREAD)
+    dma_rsrc = tile_rsrc<C>(a, b, k_issue, vis, lane, issue);
   else
     issue_tile<C>(a, dma_stage, b, k_issue, vis, wave, lane, dma_off, issue);
 
@@ -490,6 +526,23 @@ __device__ __forceinline__ void tile_step(const AttnArgs& a, unsigned char* __re
       F::acc_v(s0, av, bv);
     else
       F::acc_v_last(s0, av, bv);
+    if constexpr (SPREAD) {
+      static_assert(!SPREAD || C::RK >= 4 * (C::NINST / C::NW), "one load per four k-steps");
+      if (kb % 4 == 2) {
+        switch (kb / 4) {
+          case 0: dma_block<C, 0>(dma_rsrc, dma_stage, wave, dma_off); break;
+          case 1: dma_block<C, 1>(dma_rsrc, dma_stage, wave, dma_off); break;
+          case 2: dma_block<C, 2>(dma_rsrc, dma_stage, wave, dma_off); break;
+          case 3: dma_block<C, 3>(dma_rsrc, dma_stage, wave, dma_off); break;
+          case 4: dma_block<C, 4>(dma_rsrc, dma_stage, wave, dma_off); break;
+          case 5: dma_block<C, 5>(dma_rsrc, dma_stage, wave, dma_off); break;
+          case 6: dma_block<C, 6>(dma_rsrc, dma_stage, wave, dma_off); break;
+          case 7: dma_block<C, 7>(dma_rsrc, dma_stage, wave, dma_off); break;
+          case 8: dma_block<C, 8>(dma_rsrc, dma_stage, wave, dma_off); break;
+          default: break;
+        }
+      }
+    }
   }
 
   // ---- online softmax for head (wave*32 + l32) over the 32 tokens -------
