@@ -334,9 +334,13 @@ __device__ inline void issue_tile(const AttnArgs& a, unsigned char* stage, int b
 // padding load into the slot's spare 256 B, so that every wave issues
 // E4_LOADS loads.  Rows at or past `vis`, a page outside the pool (error
 // bit 2) and a dead tile read as zeros, as in issue_tile.
+// Buffer records of an E4M3 tile's codes and scales (page lookup and
+// visible rows), and load i of a wave (see issue_tile_e4).
+struct E4Rsrc {
+  __amdgpu_buffer_rsrc_t codes, scales;
+};
 template <class C>
-__device__ inline void issue_tile_e4(const AttnArgs& a, unsigned char* st, int b, int k, int vis, int wave, int lane,
-                                     bool live) {
+__device__ inline E4Rsrc e4_rsrc(const AttnArgs& a, int b, int k, int vis, int lane, bool live) {
   const int t0 = k * C::TILE;
   size_t row0 = 0;
   bool ok = live;
@@ -351,20 +355,28 @@ __device__ inline void issue_tile_e4(const AttnArgs& a, unsigned char* st, int b
     }
   }
   const int rows = ok ? min(max(vis - t0, 0), C::TILE) : 0;
-  const __amdgpu_buffer_rsrc_t rc = make_rsrc(reinterpret_cast<const unsigned char*>(a.pool) + row0 * C::R, rows * C::R);
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scales + row0, rows * 4);
+  return E4Rsrc{make_rsrc(reinterpret_cast<const unsigned char*>(a.pool) + row0 * C::R, rows * C::R),
+                make_rsrc(a.scales + row0, rows * 4)};
+}
+template <class C>
+__device__ inline void e4_load(const E4Rsrc& r, unsigned char* st, int wave, int lane, int i) {
   constexpr int CP = C::CNT ? 2 : 0;
+  const int j = wave + C::NW * i;  // wave-uniform
+  if (j < C::E4_BLOCKS)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.codes, MLA_LDS_PTR(st + j * 1024), 16, lane * 16, j * 1024, 0, CP);
+  else if (j == C::E4_BLOCKS)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.scales, MLA_LDS_PTR(st + C::E4_TILE), 4, lane * 4, 0, 0, CP);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(g_zero_rows, 0), MLA_LDS_PTR(st + C::E4_TILE + 256), 4, 0, 0,
+                                             0, 0);
+}
+
+template <class C>
+__device__ inline void issue_tile_e4(const AttnArgs& a, unsigned char* st, int b, int k, int vis, int wave, int lane,
+                                     bool live) {
+  const E4Rsrc r = e4_rsrc<C>(a, b, k, vis, lane, live);
 #pragma unroll
-  for (int i = 0; i < C::E4_LOADS; ++i) {
-    const int j = wave + C::NW * i;  // wave-uniform
-    if (j < C::E4_BLOCKS)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, MLA_LDS_PTR(st + j * 1024), 16, lane * 16, j * 1024, 0, CP);
-    else if (j == C::E4_BLOCKS)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, MLA_LDS_PTR(st + C::E4_TILE), 4, lane * 4, 0, 0, CP);
-    else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(g_zero_rows, 0), MLA_LDS_PTR(st + C::E4_TILE + 256), 4, 0, 0,
-                                               0, 0);
-  }
+  for (int i = 0; i < C::E4_LOADS; ++i) e4_load<C>(r, st, wave, lane, i);
 }
 
 // Converts a staged E4M3 tile into a bf16 tile slot (FAST layout), 16 codes
@@ -479,10 +491,13 @@ __device__ __forceinline__ void tile_step(const AttnArgs& a, unsigned char* __re
   // (and the page lookup) now, the nine loads spread over the score MFMAs,
   // one every four k-steps: issued back to back, the four waves' 36 loads
   // held each wave for ~600 clocks while the address unit drained them.
+  // (E4M3 tiles the same way: the code and scale records now, the loads
+  // of the staging slot spread over the first k-steps.)
   constexpr bool SPREAD = C::FAST && !C::E4;
   __amdgpu_buffer_rsrc_t dma_rsrc;
+  E4Rsrc e4r;
   if constexpr (C::E4)
-    issue_tile_e4<C>(a, dma_stage, b, k_issue, vis, wave, lane, issue);
+    e4r = e4_rsrc<C>(a, b, k_issue, vis, lane, issue);
   else if constexpr (SPREAD)
     dma_rsrc = tile_rsrc<C>(a, b, k_issue, vis, lane, issue);
   else
@@ -526,6 +541,10 @@ __device__ __forceinline__ void tile_step(const AttnArgs& a, unsigned char* __re
       F::acc_v(s0, av, bv);
     else
       F::acc_v_last(s0, av, bv);
+    if constexpr (C::E4) {
+      static_assert(!C::E4 || C::RK >= 4 * C::E4_LOADS, "one load per four k-steps");
+      if (kb % 4 == 2 && kb / 4 < C::E4_LOADS) e4_load<C>(e4r, dma_stage, wave, lane, kb / 4);
+    }
     if constexpr (SPREAD) {
       static_assert(!SPREAD || C::RK >= 4 * (C::NINST / C::NW), "one load per four k-steps");
       if (kb % 4 == 2) {
