@@ -33,6 +33,7 @@
 //     each tile column is read from LDS by exactly one wave.
 #include <math.h>
 
+#include <climits>
 #include <type_traits>
 
 #include "mla_common.h"
@@ -930,23 +931,32 @@ __device__ inline int plan_max(int v, int* wsum) {
 
 // Work plan (one block).  Streams u = v * n_hg + head group are cut into
 // 32-token tiles; every work-group gets a contiguous range of the
-// concatenated tile list.  Two ways to cut it:
+// concatenated tile list.  Three ways to cut it:
 //   * even: per0 = ceil(T / G) tiles each; ranges may span stream ends, so a
 //     work-group can run several segments (each costs a q load, a pipeline
 //     fill and a 256 KB partial write);
 //   * aligned: every stream is cut into chunks of `per` tiles with
 //     per = max(per0, ceil(T / (G - nz))) (nz: streams with tiles), which
-//     gives at most T / per + nz <= G chunks; one segment per work-group.
-// The cheaper one under (tiles + 3 x segments) on the busiest work-group is
-// used.  Outputs: srec[u] = {first tile, end tile, visible rows, 0},
+//     gives at most T / per + nz <= G chunks; one segment per work-group;
+//   * balanced: ranges of equal cost, tiles + kSegCost x stream starts
+//     (stream records staged in LDS only).
+// The one whose busiest work-group costs least in (tiles + kSegCost x
+// segments) is used; kSegCost is the measured cost of a segment in tiles
+// (per-work-group timestamps, 64 streams of 16-512 tiles: 4.6 k clocks per
+// tile, 26 k per segment).  Outputs: srec[u] = {first tile, end tile, visible rows, 0},
 // wfl[u] = {first, last work-group} (-1 for an invalid length), wrec[w] =
 // {g0, g1, first stream, its srec}.  Invalid lengths get no tiles and raise
 // error bit 4 (page ids are checked where the split kernel follows them).
+constexpr int kSegCost = 6;
+
 __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnArgs a, int cap) {
   constexpr int kLdsU = 2048;  // stream records staged in LDS up to this many streams
   __shared__ int wsum[kPlanThreads / 64];
   __shared__ int hist[1024];
   __shared__ int sx[kLdsU], sy[kLdsU];
+  __shared__ int xs[kLdsU];    // starts of the streams with tiles, in order (balanced cut)
+  __shared__ int gb[1025];     // balanced cut: work-group w gets tiles [gb[w], gb[w + 1])
+  __shared__ int jb[1025];     // ... and tile gb[w] lies in stream piece jb[w]
   const int tid = threadIdx.x;
   const int U = a.U, G = a.G, n_q = a.n_q, n_hg = a.n_hg;
   const bool staged = U <= kLdsU;
@@ -972,12 +982,13 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnArgs a, int
     }
     int tot, tot_nz;
     const int inc = plan_scan(cnt, wsum, &tot);
-    plan_scan(cnt > 0, wsum, &tot_nz);
+    const int inz = plan_scan(cnt > 0, wsum, &tot_nz);
     if (u < U) {
       reinterpret_cast<int4*>(a.srec)[u] = make_int4(carry + inc - cnt, carry + inc, vis, 0);
       if (staged) {
         sx[u] = carry + inc - cnt;
         sy[u] = carry + inc;
+        if (cnt > 0) xs[nz + inz - 1] = carry + inc - cnt;
       }
     }
     carry += tot;
@@ -1000,16 +1011,70 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnArgs a, int
   const int smax = 1 + plan_max(hmax, wsum);
   // chunks(per) <= T / per + nz, so this per yields at most G chunks
   const int per = G > nz ? max(per0, (T + (G - nz) - 1) / (G - nz)) : 0;
-  const bool aligned = per > 0 && (per + 3 <= per0 + 3 * smax);
+  // balanced cut.  Entering stream piece j (the j-th stream with tiles,
+  // tiles [xs[j], xs[j + 1])) costs kSegCost, each tile 1: the cumulative
+  // cost is F = xs[j] + kSegCost (j + 1) + (g - xs[j]) inside piece j, and
+  // its entry step spans [xs[j] + kSegCost j, xs[j] + kSegCost (j + 1)).
+  // Boundary w sits where F reaches w FT / G (FT = T + kSegCost nz): at
+  // xs[j] when that falls in piece j's entry step, else inside the piece.
+  // One thread per boundary finds its piece, the last j with
+  // xs[j] + kSegCost j <= w FT / G, and jb[w] records the piece that holds
+  // tile gb[w].
+  // Skipped when a lower bound on its cost would not beat the other cuts:
+  // the mean FT / G, and with more than two work-groups per piece FT / G
+  // plus one segment (some work-group then holds no stream start; checked
+  // on random stream mixes).
+  const long long cost_even = (long long)per0 + (long long)kSegCost * smax;
+  const long long cost_al = per > 0 ? (long long)per + kSegCost : LLONG_MAX;
+  const long long FT = (long long)T + (long long)kSegCost * nz;
+  const long long bal_lb = G > 2 * nz ? FT / G + kSegCost : (FT + G - 1) / G;
+  long long cost_bal = LLONG_MAX;
+  if (staged && G <= 1024 && nz > 0 && bal_lb + kSegCost / 2 <= min(cost_even, cost_al)) {
+    const bool narrow = FT * G < (1LL << 31);  // 32-bit division suffices
+    for (int w = tid; w <= G; w += kPlanThreads) {
+      if (w == G) {
+        gb[w] = T;
+        jb[w] = nz;
+        continue;
+      }
+      const long long t = narrow ? (long long)(w * (int)FT / G) : (long long)w * FT / G;
+      int lo = 0, hi = nz;  // xs[0] + 0 = 0 <= t
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if ((long long)xs[mid] + (long long)kSegCost * mid <= t) lo = mid; else hi = mid;
+      }
+      const long long x0 = xs[lo], x1 = lo + 1 < nz ? xs[lo + 1] : T;
+      const long long f_in = x0 + (long long)kSegCost * (lo + 1);
+      gb[w] = (int)(t < f_in ? x0 : min(x1, x0 + (t - f_in)));
+      jb[w] = lo;
+    }
+    __syncthreads();
+    int cmax = 0;
+    for (int w = tid; w < G; w += kPlanThreads) {
+      const int g0 = gb[w], g1 = gb[w + 1];
+      if (g1 > g0) {
+        // pieces holding tiles g0 and g1 - 1 (g1 at a piece start ends the previous one)
+        const int j0 = jb[w], j1 = (jb[w + 1] < nz && g1 == xs[jb[w + 1]]) || jb[w + 1] == nz ? jb[w + 1] - 1 : jb[w + 1];
+        cmax = max(cmax, g1 - g0 + kSegCost * (j1 - j0 + 1));
+      }
+    }
+    cost_bal = plan_max(cmax, wsum);
+  }
+  // (the balanced cut only when it saves at least half a segment: it may
+  // cut more streams than the others, and a close call is within the
+  // model's error)
+  // (cost_even is finite; cost_bal is LLONG_MAX when the cut was not computed)
+  const bool balanced = cost_bal <= min(cost_even, cost_al) - kSegCost / 2;
+  const bool aligned = !balanced && cost_al <= cost_even;
 
   // work-group records
   for (int w = tid; w < G; w += kPlanThreads) {
     int* wr = a.wrec + 8 * w;
     int g0 = 0, g1 = 0, u0 = 0;
     int4 r = make_int4(0, 0, 0, 0);
-    if (!aligned && w * per0 < T) {
-      g0 = w * per0;
-      g1 = min(g0 + per0, T);
+    if (balanced ? gb[w + 1] > gb[w] : (!aligned && w * per0 < T)) {
+      g0 = balanced ? gb[w] : w * per0;
+      g1 = balanced ? gb[w + 1] : min(g0 + per0, T);
       int lo = 0, hi = U;  // last stream with start <= g0 (and tiles)
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
@@ -1035,21 +1100,54 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnArgs a, int
     const int c0 = chunk_base + plan_scan(nch, wsum, &tot) - nch;
     chunk_base += tot;
     if (u < U) {
+      if (aligned && staged) xs[u] = c0;  // first chunk of stream u (xs is free again)
       int2 f = make_int2(-1, -1);
       if (r.y > r.x) {
         if (aligned) {
           f = make_int2(c0, c0 + nch - 1);
-          const int vis = reinterpret_cast<const int4*>(a.srec)[u].z;
-          for (int c = 0; c < nch; ++c) {
-            int* wr = a.wrec + 8 * (c0 + c);
-            wr[0] = r.x + c * per; wr[1] = min(r.x + (c + 1) * per, r.y); wr[2] = u;
-            wr[3] = r.x; wr[4] = r.y; wr[5] = vis;
+          if (!staged) {
+            const int vis = reinterpret_cast<const int4*>(a.srec)[u].z;
+            for (int c = 0; c < nch; ++c) {
+              int* wr = a.wrec + 8 * (c0 + c);
+              wr[0] = r.x + c * per; wr[1] = min(r.x + (c + 1) * per, r.y); wr[2] = u;
+              wr[3] = r.x; wr[4] = r.y; wr[5] = vis;
+            }
           }
+        } else if (balanced) {
+          // last work-group whose range starts at or before the stream's
+          // first / last tile (empty ranges sit before the one that holds it)
+          auto wg_of = [&](int g) {
+            int lo = 0, hi = G;  // largest w with gb[w] <= g
+            while (hi - lo > 1) {
+              const int mid = (lo + hi) >> 1;
+              if (gb[mid] <= g) lo = mid; else hi = mid;
+            }
+            return lo;
+          };
+          f = make_int2(wg_of(r.x), wg_of(r.y - 1));
         } else {
           f = make_int2(r.x / per0, (r.y - 1) / per0);
         }
       }
       reinterpret_cast<int2*>(a.wfl)[u] = f;
+    }
+  }
+  if (aligned && staged) {
+    // chunk records, one thread per work-group: its stream is the last one
+    // whose first chunk is at or before it (a stream without chunks shares
+    // its first-chunk index with the next stream, so it is never the last)
+    __syncthreads();
+    for (int w = tid; w < chunk_base; w += kPlanThreads) {
+      int lo = 0, hi = U;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (xs[mid] <= w) lo = mid; else hi = mid;
+      }
+      const int c = w - xs[lo];
+      const int vis = reinterpret_cast<const int4*>(a.srec)[lo].z;
+      int* wr = a.wrec + 8 * w;
+      wr[0] = sx[lo] + c * per; wr[1] = min(sx[lo] + (c + 1) * per, sy[lo]); wr[2] = lo;
+      wr[3] = sx[lo]; wr[4] = sy[lo]; wr[5] = vis;
     }
   }
 }
