@@ -27,8 +27,11 @@ the byte-count closed forms the pages print; ``fp8`` against
 torch.float8_e4m3fn casts, a brute-force scale search and the rounding
 error bounds (``tests/test_oracle_fp8.py``).
 
-Parity unpinned (conventions the pages leave open and both sides adopt):
-the RoPE pair layout and frequencies, the source of the query's RoPE part
-(the query latent), and the softmax scale 1/sqrt(d_nope + d_rope).
+Conventions the pages leave open, taken as readings and adopted by both
+sides: the RoPE pair layout (a relabelling of the RoPE weight columns: the
+half-split pairing on permuted columns gives the same outputs, a pin in
+``tests/test_oracle_pins.py``) and its frequencies base^(-2j/d) with the
+configured base, the source of the query's RoPE part (the query latent),
+and the softmax scale 1/sqrt(d_nope + d_rope).
 """
 from . import rope, expanded, absorbed, accounting, fp8  # noqa: F401

@@ -5,8 +5,10 @@ between the key and query factors (page "Multi-Head Latent Attention (MLA)",
 section "The RoPE problem"; page "Multi-head Latent Attention (MLA): how
 DeepSeek cuts KV cache memory", section "What MLA costs").  The reading used
 here is the original rotary form: consecutive pairs (2j, 2j+1) are rotated by
-the angle pos * base^(-2j/d).  This convention is shared with the GPU path by
-construction and is not fixed by the pages (parity unpinned for the layout).
+the angle pos * base^(-2j/d).  The pages do not fix which coordinates pair
+up; any pairing is a relabelling of the RoPE weight columns (pinned: the
+half-split pairing on permuted columns gives the same outputs), and the GPU
+path uses this one.
 """
 import numpy as np
 

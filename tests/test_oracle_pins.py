@@ -45,6 +45,39 @@ def test_pin_rope_rotation():
     assert pins.pin_rope(rope, expanded) < 1e-9
 
 
+def test_rope_pair_layout_is_a_relabelling_of_weight_columns():
+    """The pages leave RoPE's pair layout open.  Any other pairing is the
+    same family of functions: the half-split layout (pairs (j, j + d/2)) on
+    RoPE weight columns permuted into that order gives the interleaved
+    layout's output (pairs (2j, 2j + 1)) on the original columns, since a
+    score sums the rotated q_pe * k_pe products over every coordinate (page
+    "Multi-Head Latent Attention (MLA)", section "The RoPE problem": RoPE is
+    a position rotation applied to the decoupled query and key parts)."""
+    def apply_half(v, pos, base):
+        v = np.asarray(v, np.float64)
+        d = v.shape[-1]
+        ang = rope.angles(pos, d, base)
+        cos, sin = np.cos(ang), np.sin(ang)
+        a, b = v[..., : d // 2], v[..., d // 2:]
+        return np.concatenate([a * cos - b * sin, a * sin + b * cos], axis=-1)
+
+    half = types.SimpleNamespace(apply=apply_half, angles=rope.angles)
+    E2 = _mutant("expanded", "from . import rope as _rope", "from . import rope as _rope", {"_rope": half})
+    case = pins.make_case(pins.MID, 31, history="x")
+    d = pins.MID.d_rope
+    perm = np.concatenate([np.arange(0, d, 2), np.arange(1, d, 2)])  # column j <- 2j, d/2 + j <- 2j + 1
+    W2 = dict(case.weights)
+    W2["W_KR"] = np.asarray(case.weights["W_KR"])[..., perm]
+    W2["W_QR"] = np.asarray(case.weights["W_QR"])[..., perm]
+    for b in range(pins.MID.batch):
+        y1 = pins._run_decode(expanded, case, b)["y"]
+        y2 = pins._run_decode(E2, case, b, W=W2)["y"]
+        assert np.abs(y2 - y1).max() <= 1e-12 * np.abs(y1).max()
+    # and the unpermuted columns do give a different function
+    y3 = pins._run_decode(E2, case, 0)["y"]
+    assert np.abs(y3 - pins._run_decode(expanded, case, 0)["y"]).max() > 1e-3 * np.abs(y3).max()
+
+
 def test_pin_special_cases():
     assert pins.pin_special(expanded) < 1e-12
 
