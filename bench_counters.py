@@ -170,6 +170,31 @@ def trace_durations(path, skip=5):
     return [sum(per[s[k][1]][1] for s in st) / len(st) for k in range(n)]
 
 
+def trace_passes(path, warmup, k):
+    """Mean traced duration (us) of each call per bench pass: warm-up, the
+    timed region, the back-to-back steps that time the roofline call, and the
+    pass with a marker between the calls."""
+    per = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            d = int(r["Dispatch_Id"])
+            per[d] = (r["Kernel_Name"], (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    st = steps(per)
+    bounds = {"warm-up": (0, warmup), "timed": (warmup, warmup + k), "roofline": (warmup + k, warmup + 2 * k),
+              "marked": (warmup + 2 * k, warmup + 3 * k)}
+    out = {}
+    for name, (a, b) in bounds.items():
+        sel = st[a:b]
+        if not sel:
+            continue
+        tot = {c: 0.0 for c in CALLS}
+        for s_ in sel:
+            for c, d in s_:
+                tot[c] += per[d][1]
+        out[name] = {c: v / len(sel) for c, v in tot.items()}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--config", type=int, default=None, help="workload index (default: bench.py's)")
@@ -193,8 +218,10 @@ def main():
     py = sys.executable
     bench = [py, os.path.join(ROOT, "bench.py"), "--config", str(args.config), "--no-cpu-baseline",
              "--cache", args.cache] + (["--form", args.form] if args.form != "merged" else [])
+    trace_steps, trace_warmup = 20, 5
     stats_cmd = ["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d",
-                 os.path.join(args.out, "trace"), "-o", "run", "--"] + bench + ["--steps", "20", "--warmup", "5"]
+                 os.path.join(args.out, "trace"), "-o", "run", "--"] + bench + ["--steps", str(trace_steps),
+                                                                              "--warmup", str(trace_warmup)]
     if not args.summarize_only:
         run(stats_cmd, args.out, "trace", 600)
     pmc = {}
@@ -282,6 +309,13 @@ def main():
         for r in krows:
             f.write(f"{r['Name'][:90]:90s} {r['Calls']:>6s} {float(r['AverageNs']) / 1e3:10.2f} "
                     f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} {float(r['Percentage']):8.2f}\n")
+        f.write("# per bench pass: mean traced duration (us) of each call's kernels per step (warm-up; timed\n"
+                "# region; back-to-back steps with an event pair around the roofline call; pass with a marker\n"
+                "# between the calls)\n")
+        passes = trace_passes(find(args.out, "trace", "kernel_trace.csv"), trace_warmup, trace_steps)
+        f.write(f"# {'call':22s}" + "".join(f" {p:>10s}" for p in passes) + "\n")
+        for c in CALLS:
+            f.write(f"# {c:22s}" + "".join(f" {passes[p][c]:10.2f}" for p in passes) + "\n")
     with open(os.path.join(prof, f"hbm_traffic_{workload}.txt"), "w") as f:
         f.write(f"# HBM traffic per dispatch, workload {workload}, last step of a 3-step bench run\n")
         for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
